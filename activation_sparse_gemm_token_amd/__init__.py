@@ -1,0 +1,175 @@
+"""Python binding of librtlynx, the MI355X (gfx950) online 2:4
+activation-sparse linear layer.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+of ``librtlynx.so``; PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing or the device is not gfx950
+the calls raise.
+
+Entry points (same names as the C ABI in include/rtlynx.h, without the
+``rtl_`` prefix):
+
+* ``sparsify_2of4(x, fold_scale=False)`` -> (vals, idx, scale)
+* ``sparse_linear(x, w, lora_a=None, lora_b=None, lora_scale=1.0)`` -> y
+* ``dense_linear(x, w)`` -> y
+* ``sparse_linear_workspace_bytes(M, K, r)``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "RtlError", "lib", "library_path", "sparsify_2of4", "sparse_linear", "dense_linear",
+    "sparse_linear_workspace_bytes", "version", "status_string", "STATUS",
+    "FOLD_SCALE", "MAX_LORA_RANK",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "librtlynx.so")
+
+STATUS = {
+    0: "RTL_OK", 1: "RTL_ERR_NULL_POINTER", 2: "RTL_ERR_BAD_SHAPE", 3: "RTL_ERR_MISALIGNED",
+    4: "RTL_ERR_WORKSPACE", 5: "RTL_ERR_NO_DEVICE", 6: "RTL_ERR_UNSUPPORTED_ARCH",
+    7: "RTL_ERR_HIP", 8: "RTL_ERR_BAD_FLAGS",
+}
+FOLD_SCALE = 0x1
+MAX_LORA_RANK = 128
+
+_c_i64, _c_u32, _c_vp, _c_f = ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
+
+_SIGNATURES = {
+    "rtl_sparsify_2of4": (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_u32, _c_vp]),
+    "rtl_sparse_linear_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
+    "rtl_sparse_linear": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                         _c_f, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "rtl_dense_linear": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "rtl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "rtl_version": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+class RtlError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librtlynx (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"librtlynx.so is not built ({library_path}); run "
+                               "python -m activation_sparse_gemm_token_amd.build")
+        handle = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().rtl_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return lib().rtl_version()
+
+
+def sparse_linear_workspace_bytes(m: int, k: int, r: int) -> int:
+    return int(lib().rtl_sparse_linear_workspace_bytes(m, k, r))
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise RtlError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _as_2d(t, name: str):
+    torch = _torch()
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.reshape(-1, t.shape[-1]) if t.dim() != 2 else t
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def sparsify_2of4(x, fold_scale: bool = False, with_scale: bool = True):
+    """Mask, compensation scale and canonical compression of x [..., K].
+
+    Returns (vals [M, K/2] bf16, idx [M, ceil(K/8)] uint8, scale [M] fp32 or None).
+    """
+    torch = _torch()
+    x2 = _as_2d(x, "x")
+    m, k = x2.shape
+    vals = torch.empty((m, k // 2), dtype=torch.bfloat16, device=x2.device)
+    idx = torch.empty((m, (k // 4 + 1) // 2), dtype=torch.uint8, device=x2.device)
+    scale = torch.empty((m,), dtype=torch.float32, device=x2.device) if with_scale else None
+    st = lib().rtl_sparsify_2of4(x2.data_ptr(), m, k, vals.data_ptr(), idx.data_ptr(),
+                                 scale.data_ptr() if scale is not None else None,
+                                 FOLD_SCALE if fold_scale else 0, _stream())
+    _check(st, "rtl_sparsify_2of4")
+    return vals, idx, scale
+
+
+def sparse_linear(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.0, out=None, workspace=None):
+    """Y = S(X) W^T + lora_scale * ((X - S(X)) A^T) B^T for x [..., K], w [N, K],
+    lora_a [r, K], lora_b [N, r] (bf16, device).  Returns y [..., N] bf16."""
+    torch = _torch()
+    x2 = _as_2d(x, "x")
+    w2 = _as_2d(w, "w")
+    m, k = x2.shape
+    n = w2.shape[0]
+    if w2.shape[1] != k:
+        raise ValueError(f"w has {w2.shape[1]} input channels, x has {k}")
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        if lora_a is None or lora_b is None:
+            raise ValueError("lora_a and lora_b go together")
+        lora_a = _as_2d(lora_a, "lora_a")
+        lora_b = _as_2d(lora_b, "lora_b")
+        r = lora_a.shape[0]
+        if lora_a.shape[1] != k or lora_b.shape != (n, r):
+            raise ValueError(f"LoRA shapes {tuple(lora_a.shape)}, {tuple(lora_b.shape)} do not match "
+                             f"K={k}, N={n}")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x2.device)
+    need = sparse_linear_workspace_bytes(m, k, r)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
+    st = lib().rtl_sparse_linear(
+        x2.data_ptr(), w2.data_ptr(),
+        lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None,
+        m, n, k, r, float(lora_scale), y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "rtl_sparse_linear")
+    return y.reshape(*x.shape[:-1], n)
+
+
+def dense_linear(x, w, out=None):
+    """Y = X W^T on the dense matrix cores (the baseline)."""
+    torch = _torch()
+    x2 = _as_2d(x, "x")
+    w2 = _as_2d(w, "w")
+    m, k = x2.shape
+    n = w2.shape[0]
+    if w2.shape[1] != k:
+        raise ValueError(f"w has {w2.shape[1]} input channels, x has {k}")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x2.device)
+    st = lib().rtl_dense_linear(x2.data_ptr(), w2.data_ptr(), m, n, k, y.data_ptr(), _stream())
+    _check(st, "rtl_dense_linear")
+    return y.reshape(*x.shape[:-1], n)

@@ -1,0 +1,259 @@
+// Pre-pass of rtl_sparse_linear: the one kernel that reads X.
+//
+// For every token it makes the 2:4 pattern decision and Top-K selection
+// (qingkeai RT-Lynx article, sections 01 and 04), measures the kept and
+// pruned L1 mass and forms the compensation scale s (ai-feeds summary,
+// 方法 / 核心模块 1; qingkeai article, section 03.1), compresses the kept
+// values together with their 2-bit positions directly into the register
+// order of gfx950's v_smfmac_f32_16x16x64_bf16 A operand ("layout
+// generation", qingkeai article, section 04), and computes the LoRA-down
+// product of the pruned residual (qingkeai article, section 03.2):
+//
+//   T = (X - S(X)) A^T = ((1-M)*X) A^T + (1 - s) * ((M*X) A^T)
+//
+// Both terms are 2:4-sparse products of exact input words, so they run on the
+// structured-sparse matrix cores with the kept and the pruned halves of each
+// group, and no cancellation happens in fp32.  alpha*T is stored as a bf16
+// hi/lo pair in the dense 16x16x32 A-operand order for the GEMM epilogue.
+//
+// Selection happens here, once per element, and not in the GEMM prologue:
+// there it would be repeated for every N tile, and its VALU cost (about 30
+// integer instructions per group) exceeds the structured-sparse MFMA time
+// of the tile.
+//
+// Grid: one workgroup of 8 wavefronts per 16-token block; wavefront w covers
+// a contiguous range of 128-channel k-pairs.  Lane l handles token l % 16 and
+// the 16 channels (4 groups) starting at 16 * (l / 16) of each 64-channel
+// k-step, which is exactly the lane's share of the A operand.
+#include "rtl_common.hpp"
+#include "rtl_kernels.hpp"
+
+namespace rtl {
+
+namespace {
+
+constexpr int kWaves = 8;
+
+// Four groups (16 channels) of one lane: returns the kept and pruned operand
+// words and their 16-bit index fields.
+struct Quad {
+  u32x4 kept, pruned;
+  uint32_t kcode, pcode;
+};
+
+__device__ __forceinline__ void select_quad(const uint32_t (&w)[8], Quad& q, float& lk, float& lp) {
+  q.kcode = 0;
+  q.pcode = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t lo = w[2 * g], hi = w[2 * g + 1];
+    const Group4 r = rank_group(lo, hi);
+    const uint32_t ks = pair_selector_sorted(r.first, r.second);
+    const uint32_t ps = pair_selector_sorted(r.third, r.fourth);
+    q.kept[g] = __builtin_amdgcn_perm(hi, lo, ks);
+    q.pruned[g] = __builtin_amdgcn_perm(hi, lo, ps);
+    q.kcode |= code_from_selector(ks) << (4 * g);
+    q.pcode |= code_from_selector(ps) << (4 * g);
+    lk = add_mag_pair(lk, r.first, r.second);
+    lp = add_mag_pair(lp, r.third, r.fourth);
+  }
+}
+
+template <bool ALIGNED16>
+__device__ __forceinline__ void load_quad(const uint16_t* __restrict__ row_ptr, bool row_ok,
+                                          int64_t k, int64_t K, uint32_t (&w)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = 0;
+  if (!row_ok) return;
+  if constexpr (ALIGNED16) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (k + 8 * h + 8 <= K) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row_ptr + k + 8 * h);
+        w[4 * h + 0] = v[0]; w[4 * h + 1] = v[1]; w[4 * h + 2] = v[2]; w[4 * h + 3] = v[3];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (k + 4 * g + 4 <= K) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(row_ptr + k + 4 * g);
+        w[2 * g] = v[0]; w[2 * g + 1] = v[1];
+      }
+    }
+  }
+}
+
+// B operand of v_smfmac_f32_16x16x64_bf16 from a row-major [rows, K] bf16
+// matrix: lane l takes row n = n0 + l % 16 and the channels
+// k0 + 8 (l / 16) + [0, 8) and k0 + 32 + 8 (l / 16) + [0, 8).
+template <bool ALIGNED16>
+__device__ __forceinline__ bf16x16 load_b_sparse(const uint16_t* __restrict__ base, int64_t rows,
+                                                 int64_t K, int64_t n, int64_t k0, int lane) {
+  u32x8 v = (u32x8){0, 0, 0, 0, 0, 0, 0, 0};
+  if (n < rows) {
+    const uint16_t* p = base + n * K;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t k = k0 + 32 * h + 8 * (lane >> 4);
+      if constexpr (ALIGNED16) {
+        if (k + 8 <= K) {
+          const u32x4 c = *reinterpret_cast<const u32x4*>(p + k);
+          v[4 * h + 0] = c[0]; v[4 * h + 1] = c[1]; v[4 * h + 2] = c[2]; v[4 * h + 3] = c[3];
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (k + 4 * q + 4 <= K) {
+            const u32x2 c = *reinterpret_cast<const u32x2*>(p + k + 4 * q);
+            v[4 * h + 2 * q] = c[0]; v[4 * h + 2 * q + 1] = c[1];
+          }
+        }
+      }
+    }
+  }
+  return __builtin_bit_cast(bf16x16, v);
+}
+
+template <bool ALIGNED16, int NCB>
+__global__ void __launch_bounds__(64 * kWaves)
+prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora_a,
+               int64_t M, int64_t K, int64_t r, float alpha,
+               u32x4* __restrict__ xv, uint32_t* __restrict__ xi, float* __restrict__ s_out,
+               u32x4* __restrict__ t_out, int64_t kpairs, int64_t rsteps) {
+  // NCB = 16-wide column blocks of the LoRA rank covered (0: no LoRA branch).
+  constexpr int NT = NCB > 0 ? NCB : 1;
+  __shared__ float red_l[kWaves][2][16];
+  __shared__ float s_sh[16];
+  __shared__ float red_t[NCB > 0 ? kWaves : 1][16][NT * 16 + 1];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t mb = blockIdx.x;
+  const int64_t row = mb * 16 + (lane & 15);
+  const bool row_ok = row < M;
+  const uint16_t* row_ptr = x + (row_ok ? row : 0) * K;
+  const int64_t ksteps = 2 * kpairs;
+
+  float lk = 0.f, lp = 0.f;
+  f32x4 tk[NT], tp[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) { tk[c] = (f32x4){0, 0, 0, 0}; tp[c] = (f32x4){0, 0, 0, 0}; }
+
+  const int64_t p_begin = (int64_t)wave * kpairs / kWaves;
+  const int64_t p_end = (int64_t)(wave + 1) * kpairs / kWaves;
+  for (int64_t p = p_begin; p < p_end; ++p) {
+    uint32_t w0[8], w1[8];
+    const int64_t ks0 = 2 * p;
+    load_quad<ALIGNED16>(row_ptr, row_ok, ks0 * 64 + 16 * (lane >> 4), K, w0);
+    load_quad<ALIGNED16>(row_ptr, row_ok, ks0 * 64 + 64 + 16 * (lane >> 4), K, w1);
+    Quad q0, q1;
+    select_quad(w0, q0, lk, lp);
+    select_quad(w1, q1, lk, lp);
+    const int64_t grp = mb >> 3, sub = mb & 7;
+    xv[((grp * ksteps + ks0) * 8 + sub) * 64 + lane] = q0.kept;
+    xv[((grp * ksteps + ks0 + 1) * 8 + sub) * 64 + lane] = q1.kept;
+    xi[((grp * kpairs + p) * 8 + sub) * 64 + lane] = q0.kcode | (q1.kcode << 16);
+    if constexpr (NCB > 0) {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const int64_t n = c * 16 + (lane & 15);
+        const bf16x16 b0 = load_b_sparse<ALIGNED16>(lora_a, r, K, n, ks0 * 64, lane);
+        const bf16x16 b1 = load_b_sparse<ALIGNED16>(lora_a, r, K, n, ks0 * 64 + 64, lane);
+        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.kept), b0, tk[c], (int)q0.kcode, 0, 0);
+        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.pruned), b0, tp[c], (int)q0.pcode, 0, 0);
+        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.kept), b1, tk[c], (int)q1.kcode, 0, 0);
+        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.pruned), b1, tp[c], (int)q1.pcode, 0, 0);
+      }
+    }
+  }
+
+  // Per-token L1 sums: lanes l, l^16, l^32, l^48 share a token; then across
+  // wavefronts in a fixed order.
+  lk += __shfl_xor(lk, 16, 64);
+  lk += __shfl_xor(lk, 32, 64);
+  lp += __shfl_xor(lp, 16, 64);
+  lp += __shfl_xor(lp, 32, 64);
+  if (lane < 16) { red_l[wave][0][lane] = lk; red_l[wave][1][lane] = lp; }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) { a += red_l[w][0][threadIdx.x]; b += red_l[w][1][threadIdx.x]; }
+    const float s = a > 0.f ? (a + b) / a : 1.0f;
+    s_sh[threadIdx.x] = s;
+    s_out[mb * 16 + threadIdx.x] = s;
+  }
+  if constexpr (NCB > 0) {
+    __syncthreads();
+    // Accumulator layout of a 16x16 block: lane l holds column l % 16 of rows
+    // 4 (l / 16) + i.  T_w = T_pruned + (1 - s) T_kept per wavefront, then
+    // summed over wavefronts in a fixed order.
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * (lane >> 4) + i;
+        red_t[wave][rr][c * 16 + (lane & 15)] = tp[c][i] + (1.0f - s_sh[rr]) * tk[c][i];
+      }
+    }
+    __syncthreads();
+    // Output fragment (rs, l): token l % 16, rank columns 32 rs + 8 (l / 16) + [0, 8).
+    const int64_t frag = threadIdx.x;
+    if (frag < rsteps * 64) {
+      const int rs = (int)(frag >> 6), fl = (int)(frag & 63);
+      const int rr = fl & 15;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        float v[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int col = 32 * rs + 8 * (fl >> 4) + j + e;
+          float a = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) a += red_t[w][rr][col];
+          v[e] = alpha * a;
+        }
+        const uint32_t h = pack_bf16x2(v[0], v[1]);
+        hi[j / 2] = h;
+        lo[j / 2] = pack_bf16x2(v[0] - bf16_lo_to_f32(h), v[1] - bf16_hi_to_f32(h));
+      }
+      t_out[((mb * rsteps + rs) * 2 + 0) * 64 + fl] = (u32x4){hi[0], hi[1], hi[2], hi[3]};
+      t_out[((mb * rsteps + rs) * 2 + 1) * 64 + fl] = (u32x4){lo[0], lo[1], lo[2], lo[3]};
+    }
+  }
+}
+
+template <bool A16>
+hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M, int64_t K,
+                            int64_t r, float alpha, const WsLayout& L, char* ws, hipStream_t stream) {
+  const dim3 grid((unsigned)(L.mp / 16)), block(64 * kWaves);
+  u32x4* xv = reinterpret_cast<u32x4*>(ws + L.off_xv);
+  uint32_t* xi = reinterpret_cast<uint32_t*>(ws + L.off_xi);
+  float* s = reinterpret_cast<float*>(ws + L.off_s);
+  u32x4* t = reinterpret_cast<u32x4*>(ws + L.off_t);
+  const int64_t kpairs = L.kp / 128, rsteps = L.rp / 32;
+  const int ncb = (int)(L.rp / 16);
+  if (r == 0)
+    prepass_kernel<A16, 0><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, 0);
+  else if (ncb <= 2)
+    prepass_kernel<A16, 2><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, rsteps);
+  else if (ncb <= 4)
+    prepass_kernel<A16, 4><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, rsteps);
+  else
+    prepass_kernel<A16, 8><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, rsteps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prepass(const uint16_t* x, const uint16_t* lora_a, int64_t M, int64_t K,
+                          int64_t r, float lora_scale, void* workspace, hipStream_t stream) {
+  const WsLayout L = ws_layout(M, K, r);
+  char* ws = static_cast<char*>(workspace);
+  if (K % 8 == 0) return launch_prepass_t<true>(x, lora_a, M, K, r, lora_scale, L, ws, stream);
+  return launch_prepass_t<false>(x, lora_a, M, K, r, lora_scale, L, ws, stream);
+}
+
+}  // namespace rtl

@@ -1,0 +1,26 @@
+// Launch wrappers of librtlynx's kernels (internal; the public interface is
+// include/rtlynx.h).  Each returns hipGetLastError() after its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rtl {
+
+hipError_t launch_sparsify_2of4(const uint16_t* x, int64_t M, int64_t K, uint16_t* vals,
+                                uint8_t* idx, float* scale, bool fold, hipStream_t stream);
+
+// Pre-pass of the fused path: selection, compression into the structured-
+// sparse matrix-core operand order, per-token scale, LoRA-down product.
+hipError_t launch_prepass(const uint16_t* x, const uint16_t* lora_a, int64_t M, int64_t K,
+                          int64_t r, float lora_scale, void* workspace, hipStream_t stream);
+
+// Sparse GEMM on the compressed operand plus the scale and LoRA-up epilogue.
+hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const uint16_t* lora_b,
+                              int64_t M, int64_t N, int64_t K, int64_t r, uint16_t* y,
+                              hipStream_t stream);
+
+hipError_t launch_dense_gemm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
+                             int64_t K, uint16_t* y, hipStream_t stream);
+
+}  // namespace rtl

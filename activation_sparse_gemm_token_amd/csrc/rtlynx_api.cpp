@@ -1,0 +1,132 @@
+// Host side of librtlynx: argument validation, device checks and launches
+// behind the C ABI declared in include/rtlynx.h.
+//
+// Validation is pure arithmetic on the arguments and runs before any HIP
+// call, so an invalid call touches neither the device nor the runtime's
+// error state.  The only process-wide state is a per-device cache of the
+// "is this a gfx950" answer.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "rtl_common.hpp"
+#include "rtl_kernels.hpp"
+#include "rtlynx.h"
+
+#define RTL_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kVersion = 10000;            // 1.0.0
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dims_ok(int64_t M, int64_t K) {
+  return M >= 0 && K >= 4 && K % 4 == 0 && M < kMaxDim && K < kMaxDim;
+}
+
+rtl_status check_device() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return RTL_ERR_NO_DEVICE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return RTL_ERR_NO_DEVICE;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return RTL_ERR_UNSUPPORTED_ARCH;
+  int known = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return RTL_ERR_HIP;
+    }
+    known = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(known, std::memory_order_relaxed);
+  }
+  return known == 1 ? RTL_OK : RTL_ERR_UNSUPPORTED_ARCH;
+}
+
+rtl_status from_hip(hipError_t e) { return e == hipSuccess ? RTL_OK : RTL_ERR_HIP; }
+
+}  // namespace
+
+RTL_API rtl_status rtl_sparsify_2of4(const uint16_t* x, int64_t M, int64_t K, uint16_t* vals,
+                                     uint8_t* idx, float* scale, uint32_t flags, void* hip_stream) {
+  if (!dims_ok(M, K)) return RTL_ERR_BAD_SHAPE;
+  if ((flags & ~RTL_FOLD_SCALE) != 0) return RTL_ERR_BAD_FLAGS;
+  if (M == 0) return RTL_OK;
+  if (x == nullptr || vals == nullptr || idx == nullptr) return RTL_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(vals) || !aligned16(idx) || (scale != nullptr && !aligned16(scale)))
+    return RTL_ERR_MISALIGNED;
+  const rtl_status d = check_device();
+  if (d != RTL_OK) return d;
+  return from_hip(rtl::launch_sparsify_2of4(x, M, K, vals, idx, scale, (flags & RTL_FOLD_SCALE) != 0,
+                                            static_cast<hipStream_t>(hip_stream)));
+}
+
+RTL_API size_t rtl_sparse_linear_workspace_bytes(int64_t M, int64_t K, int64_t r) {
+  if (!dims_ok(M, K) || r < 0 || r > RTL_MAX_LORA_RANK) return 0;
+  if (M == 0) return 0;
+  return rtl::ws_layout(M, K, r).total;
+}
+
+RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const uint16_t* lora_a,
+                                     const uint16_t* lora_b, int64_t M, int64_t N, int64_t K,
+                                     int64_t r, float lora_scale, uint16_t* y, void* workspace,
+                                     size_t workspace_bytes, void* hip_stream) {
+  if (!dims_ok(M, K) || N < 0 || N >= kMaxDim || r < 0 || r > RTL_MAX_LORA_RANK) return RTL_ERR_BAD_SHAPE;
+  if (M == 0 || N == 0) return RTL_OK;
+  if (x == nullptr || w == nullptr || y == nullptr) return RTL_ERR_NULL_POINTER;
+  if (r > 0 && (lora_a == nullptr || lora_b == nullptr)) return RTL_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return RTL_ERR_MISALIGNED;
+  if (r > 0 && (!aligned16(lora_a) || !aligned16(lora_b))) return RTL_ERR_MISALIGNED;
+  const size_t need = rtl::ws_layout(M, K, r).total;
+  if (workspace == nullptr || workspace_bytes < need) return RTL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
+  const rtl_status d = check_device();
+  if (d != RTL_OK) return d;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const uint16_t* a = r > 0 ? lora_a : nullptr;
+  const uint16_t* b = r > 0 ? lora_b : nullptr;
+  hipError_t e = rtl::launch_prepass(x, a, M, K, r, lora_scale, workspace, stream);
+  if (e != hipSuccess) return RTL_ERR_HIP;
+  e = rtl::launch_sparse_gemm(workspace, w, b, M, N, K, r, y, stream);
+  return from_hip(e);
+}
+
+RTL_API rtl_status rtl_dense_linear(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
+                                    int64_t K, uint16_t* y, void* hip_stream) {
+  if (!dims_ok(M, K) || N < 0 || N >= kMaxDim) return RTL_ERR_BAD_SHAPE;
+  if (M == 0 || N == 0) return RTL_OK;
+  if (x == nullptr || w == nullptr || y == nullptr) return RTL_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return RTL_ERR_MISALIGNED;
+  const rtl_status d = check_device();
+  if (d != RTL_OK) return d;
+  return from_hip(rtl::launch_dense_gemm(x, w, M, N, K, y, static_cast<hipStream_t>(hip_stream)));
+}
+
+RTL_API const char* rtl_status_string(rtl_status s) {
+  switch (s) {
+    case RTL_OK: return "ok";
+    case RTL_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case RTL_ERR_BAD_SHAPE: return "invalid shape (sizes must be >= 0, K >= 4 and K % 4 == 0, r <= RTL_MAX_LORA_RANK)";
+    case RTL_ERR_MISALIGNED: return "a base pointer is not 16-byte aligned";
+    case RTL_ERR_WORKSPACE: return "workspace missing or smaller than rtl_sparse_linear_workspace_bytes()";
+    case RTL_ERR_NO_DEVICE: return "no HIP device is visible";
+    case RTL_ERR_UNSUPPORTED_ARCH: return "the current device is not gfx950 (MI355X)";
+    case RTL_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case RTL_ERR_BAD_FLAGS: return "unknown flag bits";
+  }
+  return "unknown status";
+}
+
+RTL_API int rtl_version(void) { return kVersion; }

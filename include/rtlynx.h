@@ -1,0 +1,153 @@
+/*
+ * rtlynx.h - C ABI of librtlynx, an online 2:4 activation-sparse linear layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (RT-Lynx, arXiv 2605.26632):
+ *
+ *   Y = S(X) W^T + alpha * ((X - S(X)) A^T) B^T
+ *
+ * S(X) is computed online, per token (row of X):
+ *   - in every group of 4 consecutive input channels the two entries of
+ *     largest magnitude are kept and the other two are pruned
+ *     (ai-feeds summary, section 方法 / 输入与稀疏化策略: a 2:4 pattern on the
+ *     activations; qingkeai article, section 01: 2 non-zeros in every 4
+ *     consecutive elements; section 03.1: Top-K selection).  Equal magnitudes
+ *     are resolved toward the lower channel index, so the kept set is unique;
+ *   - the kept entries are multiplied by s = (L1 of the row) / (L1 of the
+ *     kept entries), which hands the pruned L1 mass back to the kept values in
+ *     proportion to their magnitude (ai-feeds summary, 方法 / 核心模块 1,
+ *     norm-compensated sparsification; qingkeai article, section 03.1).
+ *     s = 1 for an all-zero row;
+ *   - W is the dense frozen weight (qingkeai article, section 02:
+ *     Y = S(X) W^T); the rank-r LoRA branch (A, B) acts on the pruned
+ *     residual X - S(X) (qingkeai article, section 03.2; rank 64 in the
+ *     neuraltrendhub summary, "What the paper found").
+ *
+ * Common conventions for every entry point:
+ *   - bf16 tensors are passed as raw 16-bit words (uint16_t), row-major,
+ *     densely packed (row stride = number of columns).
+ *   - Every tensor pointer is device memory owned by the caller.  The library
+ *     allocates nothing and keeps no pointer after a call returns.
+ *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise.  Outputs must not alias inputs.
+ *   - Every base pointer must be 16-byte aligned.
+ *   - Arguments are validated before any HIP call; on error nothing is
+ *     launched and nothing is written.  The library keeps no sticky error
+ *     state: a failed call leaves it usable.
+ *   - Only gfx950 devices are supported: any other device gives
+ *     RTL_ERR_UNSUPPORTED_ARCH, no device gives RTL_ERR_NO_DEVICE.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef RTLYNX_H
+#define RTLYNX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RTL_OK = 0,
+  RTL_ERR_NULL_POINTER = 1,      /* a required pointer is NULL              */
+  RTL_ERR_BAD_SHAPE = 2,         /* negative size, K % 4 != 0, K == 0, ...  */
+  RTL_ERR_MISALIGNED = 3,        /* a base pointer is not 16-byte aligned    */
+  RTL_ERR_WORKSPACE = 4,         /* workspace missing or too small           */
+  RTL_ERR_NO_DEVICE = 5,         /* no HIP device is visible                 */
+  RTL_ERR_UNSUPPORTED_ARCH = 6,  /* the current device is not gfx950         */
+  RTL_ERR_HIP = 7,               /* a HIP runtime call or launch failed      */
+  RTL_ERR_BAD_FLAGS = 8          /* unknown bits in a flags argument         */
+} rtl_status;
+
+/* rtl_sparsify_2of4 flag: store vals = bf16_rne(s * x) (the compensated
+ * values) instead of exact copies of x. */
+#define RTL_FOLD_SCALE 0x1u
+
+/* Largest LoRA rank the fused path accepts. */
+#define RTL_MAX_LORA_RANK 128
+
+/*
+ * rtl_sparsify_2of4 - mask, compensation scale and compression of X.
+ *
+ * The 2:4 pattern decision, Top-K selection and activation compression of the
+ * fused path (qingkeai article, section 04), written out to HBM in the
+ * library's canonical compressed format:
+ *
+ *   x      [M, K]            bf16, input activations, K % 4 == 0, K >= 4.
+ *   vals   [M, K/2]          bf16, output: group g's two kept words at
+ *                            columns 2g and 2g+1, lower channel first; exact
+ *                            copies of x unless flags has RTL_FOLD_SCALE.
+ *   idx    [M, ceil(K/8)]    uint8, output: group g's code
+ *                            idx0 | idx1 << 2 (idx0 < idx1 the kept in-group
+ *                            positions) in byte g/2, low nibble for even g,
+ *                            high nibble for odd g; when K/4 is odd the last
+ *                            byte's high nibble is 0.
+ *   scale  [M]               fp32, output, may be NULL: the per-token s.
+ *   flags                    0 or RTL_FOLD_SCALE.
+ *
+ * M == 0 is a no-op.  The base pointers x, vals, idx and scale (when not
+ * NULL) must be 16-byte aligned; rows of vals and idx need not be.
+ */
+rtl_status rtl_sparsify_2of4(const uint16_t* x, int64_t M, int64_t K,
+                             uint16_t* vals, uint8_t* idx, float* scale,
+                             uint32_t flags, void* hip_stream);
+
+/*
+ * rtl_sparse_linear_workspace_bytes - device workspace rtl_sparse_linear needs
+ * for M tokens, K input channels and LoRA rank r (the compressed activation in
+ * the matrix-core operand order, the per-token scale and the LoRA-down
+ * product).  Returns 0 for invalid sizes.
+ */
+size_t rtl_sparse_linear_workspace_bytes(int64_t M, int64_t K, int64_t r);
+
+/*
+ * rtl_sparse_linear - the fused online 2:4 activation-sparse linear layer:
+ * pattern decision, Top-K, compression, sparse GEMM on the structured-sparse
+ * matrix cores, and the LoRA residual branch (qingkeai article, sections 02,
+ * 03 and 04).
+ *
+ *   x         [M, K]   bf16 activations (tokens x input channels).
+ *   w         [N, K]   bf16 dense frozen weight (nn.Linear layout).
+ *   lora_a    [r, K]   bf16 LoRA down factor; required when r > 0,
+ *                      ignored when r == 0.
+ *   lora_b    [N, r]   bf16 LoRA up factor; same rule as lora_a.
+ *   lora_scale         alpha, multiplies the LoRA branch.
+ *   y         [M, N]   bf16 output, fp32 accumulation rounded to nearest even.
+ *   workspace          device scratch of at least
+ *                      rtl_sparse_linear_workspace_bytes(M, K, r) bytes,
+ *                      16-byte aligned.  Its contents are overwritten.
+ *
+ * K % 4 == 0, K >= 4, 0 <= r <= RTL_MAX_LORA_RANK.  M == 0 or N == 0 is a
+ * no-op.  M, N and K need not be tile multiples.
+ */
+rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w,
+                             const uint16_t* lora_a, const uint16_t* lora_b,
+                             int64_t M, int64_t N, int64_t K, int64_t r,
+                             float lora_scale, uint16_t* y,
+                             void* workspace, size_t workspace_bytes,
+                             void* hip_stream);
+
+/*
+ * rtl_dense_linear - the dense baseline Y = X W^T (the denominator of the
+ * speedups the pages quote, qingkeai article, section 05), bf16 inputs, fp32
+ * accumulation on the dense matrix cores, bf16 output rounded to nearest even.
+ *
+ *   x [M, K], w [N, K], y [M, N].  K % 4 == 0, K >= 4.  M == 0 or N == 0 is
+ *   a no-op.
+ */
+rtl_status rtl_dense_linear(const uint16_t* x, const uint16_t* w,
+                            int64_t M, int64_t N, int64_t K,
+                            uint16_t* y, void* hip_stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* rtl_status_string(rtl_status s);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int rtl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTLYNX_H */

@@ -1,0 +1,159 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every
+symbol include/rtlynx.h declares, and rejects every invalid argument with its
+documented status before any HIP call.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import activation_sparse_gemm_token_amd as rtl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtlynx.h")
+
+OK, NULLP, SHAPE, MISAL, WS, NODEV, ARCH, HIP, FLAGS = range(9)
+P = 0x10000          # fake, 16-byte aligned "device" addresses: never dereferenced
+P2 = 0x20000
+P3 = 0x30000
+P4 = 0x40000
+P5 = 0x50000
+WSP = 0x60000
+BIG = 1 << 40
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(rtl_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = rtl.lib()
+    syms = _declared_symbols()
+    assert set(syms) >= {"rtl_sparsify_2of4", "rtl_sparse_linear", "rtl_dense_linear",
+                         "rtl_sparse_linear_workspace_bytes", "rtl_status_string", "rtl_version"}
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_only_declared_symbols_are_exported():
+    """-fvisibility=hidden: the C ABI is the whole dynamic interface."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", rtl.library_path], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    rtl_syms = {s for s in exported if s.startswith("rtl_")}
+    assert rtl_syms == set(_declared_symbols())
+
+
+def test_version_and_status_strings():
+    assert rtl.version() == 10000
+    for code in range(9):
+        s = rtl.status_string(code)
+        assert isinstance(s, str) and s
+    assert rtl.status_string(OK) == "ok"
+    assert rtl.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    # rows padded to 256, K to 128, r to 32; regions 256-byte aligned
+    def expect(m, k, r):
+        mp, kp, rp = -(-m // 256) * 256, -(-k // 128) * 128, -(-r // 32) * 32
+        up = lambda v: -(-v // 256) * 256
+        o = up(mp * kp)
+        o = up(o + mp * kp // 32)
+        o = up(o + mp * 4)
+        return up(o + mp * rp * 4)
+    for m, k, r in [(1, 4, 0), (64, 256, 8), (4096, 3072, 64), (9216, 3072, 64), (300, 516, 24), (257, 1000, 5)]:
+        assert rtl.sparse_linear_workspace_bytes(m, k, r) == expect(m, k, r)
+    assert rtl.sparse_linear_workspace_bytes(0, 256, 8) == 0
+    for bad in [(-1, 256, 8), (64, 6, 8), (64, 0, 8), (64, 256, -1), (64, 256, 129), (64, 2, 0)]:
+        assert rtl.sparse_linear_workspace_bytes(*bad) == 0
+
+
+def _sl(x=P, w=P2, a=P3, b=P4, m=64, n=128, k=256, r=8, alpha=1.0, y=P5, ws=WSP, wsb=BIG, stream=None):
+    return rtl.lib().rtl_sparse_linear(x, w, a, b, m, n, k, r, alpha, y, ws, wsb, stream)
+
+
+def _sp(x=P, m=64, k=256, vals=P2, idx=P3, scale=P4, flags=0, stream=None):
+    return rtl.lib().rtl_sparsify_2of4(x, m, k, vals, idx, scale, flags, stream)
+
+
+def _dl(x=P, w=P2, m=64, n=128, k=256, y=P3, stream=None):
+    return rtl.lib().rtl_dense_linear(x, w, m, n, k, y, stream)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=6), SHAPE), (dict(k=0), SHAPE), (dict(k=2), SHAPE), (dict(m=-1), SHAPE),
+    (dict(n=-5), SHAPE), (dict(r=-1), SHAPE), (dict(r=129), SHAPE), (dict(k=1 << 31), SHAPE),
+    (dict(x=None), NULLP), (dict(w=None), NULLP), (dict(y=None), NULLP),
+    (dict(a=None), NULLP), (dict(b=None), NULLP),
+    (dict(x=P + 8), MISAL), (dict(w=P2 + 2), MISAL), (dict(y=P5 + 4), MISAL),
+    (dict(a=P3 + 8), MISAL), (dict(b=P4 + 8), MISAL),
+    (dict(ws=None), WS), (dict(wsb=1024), WS), (dict(ws=WSP + 8), MISAL),
+    (dict(m=0), OK), (dict(n=0), OK), (dict(m=0, x=None, y=None), OK),
+])
+def test_sparse_linear_rejects_invalid_arguments(kw, status):
+    assert _sl(**kw) == status
+
+
+def test_sparse_linear_workspace_exact_size_passes_validation():
+    need = rtl.sparse_linear_workspace_bytes(64, 256, 8)
+    st = _sl(wsb=need - 1)
+    assert st == WS
+    if _no_gpu():
+        assert _sl(wsb=need) == NODEV
+
+
+def test_sparse_linear_r0_ignores_lora_pointers():
+    if _no_gpu():
+        assert _sl(r=0, a=None, b=None) == NODEV
+        assert _sl(r=0, a=P3 + 8, b=None) == NODEV     # ignored, so not MISALIGNED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=6), SHAPE), (dict(m=-1), SHAPE), (dict(k=0), SHAPE),
+    (dict(x=None), NULLP), (dict(vals=None), NULLP), (dict(idx=None), NULLP),
+    (dict(x=P + 8), MISAL), (dict(vals=P2 + 4), MISAL), (dict(idx=P3 + 1), MISAL), (dict(scale=P4 + 4), MISAL),
+    (dict(flags=2), FLAGS), (dict(flags=0xFFFF), FLAGS),
+    (dict(m=0), OK), (dict(m=0, x=None), OK),
+])
+def test_sparsify_rejects_invalid_arguments(kw, status):
+    assert _sp(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=6), SHAPE), (dict(m=-1), SHAPE), (dict(n=-1), SHAPE),
+    (dict(x=None), NULLP), (dict(w=None), NULLP), (dict(y=None), NULLP),
+    (dict(x=P + 8), MISAL), (dict(w=P2 + 8), MISAL), (dict(y=P3 + 2), MISAL),
+    (dict(m=0), OK), (dict(n=0), OK),
+])
+def test_dense_linear_rejects_invalid_arguments(kw, status):
+    assert _dl(**kw) == status
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+def test_valid_calls_without_a_device_report_no_device():
+    """With valid arguments the only thing missing here is the GPU."""
+    if not _no_gpu():
+        pytest.skip("a GPU is present: valid calls would launch on fake pointers")
+    assert _sp() == NODEV
+    assert _sp(scale=None, flags=1) == NODEV
+    assert _sl() == NODEV
+    assert _dl() == NODEV
+    # the library stays usable after errors
+    assert _sl(k=6) == SHAPE
+    assert _sl() == NODEV
+
+
+def test_python_wrappers_reject_bad_tensors():
+    import torch
+    x = torch.zeros(4, 8, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        rtl.sparse_linear(x, x)
+    xb = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rtl.dense_linear(xb, xb)          # host tensors
