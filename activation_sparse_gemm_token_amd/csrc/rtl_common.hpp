@@ -42,7 +42,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t M, int64_t K, int64_t r) {
   size_t o = 0;
   L.off_xv = o; o += (size_t)L.mp * (size_t)L.kp;                 // (mp/16)(kp/64) x 1 KiB
   o = (size_t)round_up((int64_t)o, 256);
-  L.off_xi = o; o += (size_t)L.mp * (size_t)L.kp / 32;            // (mp/16)(kp/128) x 256 B
+  L.off_xi = o; o += (size_t)L.mp * (size_t)L.kp / 8;             // (mp/16)(kp/128) x 64 lanes x 4 B
   o = (size_t)round_up((int64_t)o, 256);
   L.off_s = o; o += (size_t)L.mp * 4;
   o = (size_t)round_up((int64_t)o, 256);

@@ -60,7 +60,7 @@ def test_workspace_bytes():
         mp, kp, rp = -(-m // 256) * 256, -(-k // 128) * 128, -(-r // 32) * 32
         up = lambda v: -(-v // 256) * 256
         o = up(mp * kp)
-        o = up(o + mp * kp // 32)
+        o = up(o + mp * kp // 8)
         o = up(o + mp * 4)
         return up(o + mp * rp * 4)
     for m, k, r in [(1, 4, 0), (64, 256, 8), (4096, 3072, 64), (9216, 3072, 64), (300, 516, 24), (257, 1000, 5)]:
