@@ -11,6 +11,8 @@ Entry points (same names as the C ABI in include/rtlynx.h, without the
 
 * ``sparsify_2of4(x, fold_scale=False)`` -> (vals, idx, scale)
 * ``sparse_linear(x, w, lora_a=None, lora_b=None, lora_scale=1.0)`` -> y
+* ``prepare(x, lora_a=None, lora_scale=1.0)`` -> Prepared, ``apply(prepared, w, lora_b=None)`` -> y
+  (the two halves of sparse_linear)
 * ``dense_linear(x, w)`` -> y
 * ``sparse_linear_workspace_bytes(M, K, r)``
 """
@@ -21,7 +23,7 @@ import os
 
 __all__ = [
     "RtlError", "lib", "library_path", "sparsify_2of4", "sparse_linear", "dense_linear",
-    "sparse_linear_workspace_bytes", "version", "status_string", "STATUS",
+    "sparse_linear_workspace_bytes", "version", "status_string", "STATUS", "prepare", "apply", "Prepared",
     "FOLD_SCALE", "MAX_LORA_RANK",
 ]
 
@@ -43,6 +45,10 @@ _SIGNATURES = {
     "rtl_sparse_linear_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "rtl_sparse_linear": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                          _c_f, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "rtl_sparse_linear_prepare": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_f, _c_vp,
+                                                 ctypes.c_size_t, _c_vp]),
+    "rtl_sparse_linear_apply": (ctypes.c_int, [_c_vp, ctypes.c_size_t, _c_vp, _c_vp, _c_i64, _c_i64,
+                                               _c_i64, _c_i64, _c_vp, _c_vp]),
     "rtl_dense_linear": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
     "rtl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rtl_version": (ctypes.c_int, []),
@@ -158,6 +164,56 @@ def sparse_linear(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.0, out=N
         m, n, k, r, float(lora_scale), y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "rtl_sparse_linear")
     return y.reshape(*x.shape[:-1], n)
+
+
+class Prepared:
+    """Workspace filled by ``prepare``: the compressed activation, the
+    per-token scale and the LoRA-down product of one x, reusable by ``apply``
+    against any number of weights with the same K."""
+
+    def __init__(self, workspace, m: int, k: int, r: int, lead_shape):
+        self.workspace, self.m, self.k, self.r, self.lead_shape = workspace, m, k, r, lead_shape
+
+
+def prepare(x, lora_a=None, lora_scale: float = 1.0, workspace=None) -> Prepared:
+    """First half of sparse_linear: reads x once (rtl_sparse_linear_prepare)."""
+    torch = _torch()
+    x2 = _as_2d(x, "x")
+    m, k = x2.shape
+    r = 0
+    if lora_a is not None:
+        lora_a = _as_2d(lora_a, "lora_a")
+        r = lora_a.shape[0]
+        if lora_a.shape[1] != k:
+            raise ValueError(f"lora_a has {lora_a.shape[1]} input channels, x has {k}")
+    need = sparse_linear_workspace_bytes(m, k, r)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
+    st = lib().rtl_sparse_linear_prepare(x2.data_ptr(), lora_a.data_ptr() if r else None, m, k, r,
+                                         float(lora_scale), workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "rtl_sparse_linear_prepare")
+    return Prepared(workspace, m, k, r, tuple(x.shape[:-1]))
+
+
+def apply(prep: Prepared, w, lora_b=None, out=None):
+    """Second half of sparse_linear: sparse GEMM + scale + LoRA-up (rtl_sparse_linear_apply)."""
+    torch = _torch()
+    w2 = _as_2d(w, "w")
+    n = w2.shape[0]
+    if w2.shape[1] != prep.k:
+        raise ValueError(f"w has {w2.shape[1]} input channels, the prepared x has {prep.k}")
+    if prep.r:
+        if lora_b is None:
+            raise ValueError("the prepared x carries a LoRA branch: lora_b is required")
+        lora_b = _as_2d(lora_b, "lora_b")
+        if tuple(lora_b.shape) != (n, prep.r):
+            raise ValueError(f"lora_b must be [{n}, {prep.r}], got {tuple(lora_b.shape)}")
+    y = out if out is not None else torch.empty((prep.m, n), dtype=torch.bfloat16, device=w2.device)
+    st = lib().rtl_sparse_linear_apply(prep.workspace.data_ptr(), prep.workspace.numel(), w2.data_ptr(),
+                                       lora_b.data_ptr() if prep.r else None, prep.m, n, prep.k, prep.r,
+                                       y.data_ptr(), _stream())
+    _check(st, "rtl_sparse_linear_apply")
+    return y.reshape(*prep.lead_shape, n)
 
 
 def dense_linear(x, w, out=None):

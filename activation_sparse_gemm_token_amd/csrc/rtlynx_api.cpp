@@ -79,6 +79,39 @@ RTL_API size_t rtl_sparse_linear_workspace_bytes(int64_t M, int64_t K, int64_t r
   return rtl::ws_layout(M, K, r).total;
 }
 
+RTL_API rtl_status rtl_sparse_linear_prepare(const uint16_t* x, const uint16_t* lora_a, int64_t M,
+                                             int64_t K, int64_t r, float lora_scale, void* workspace,
+                                             size_t workspace_bytes, void* hip_stream) {
+  if (!dims_ok(M, K) || r < 0 || r > RTL_MAX_LORA_RANK) return RTL_ERR_BAD_SHAPE;
+  if (M == 0) return RTL_OK;
+  if (x == nullptr) return RTL_ERR_NULL_POINTER;
+  if (r > 0 && lora_a == nullptr) return RTL_ERR_NULL_POINTER;
+  if (!aligned16(x) || (r > 0 && !aligned16(lora_a))) return RTL_ERR_MISALIGNED;
+  if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
+  const rtl_status d = check_device();
+  if (d != RTL_OK) return d;
+  return from_hip(rtl::launch_prepass(x, r > 0 ? lora_a : nullptr, M, K, r, lora_scale, workspace,
+                                      static_cast<hipStream_t>(hip_stream)));
+}
+
+RTL_API rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspace_bytes,
+                                           const uint16_t* w, const uint16_t* lora_b, int64_t M,
+                                           int64_t N, int64_t K, int64_t r, uint16_t* y,
+                                           void* hip_stream) {
+  if (!dims_ok(M, K) || N < 0 || N >= kMaxDim || r < 0 || r > RTL_MAX_LORA_RANK) return RTL_ERR_BAD_SHAPE;
+  if (M == 0 || N == 0) return RTL_OK;
+  if (w == nullptr || y == nullptr) return RTL_ERR_NULL_POINTER;
+  if (r > 0 && lora_b == nullptr) return RTL_ERR_NULL_POINTER;
+  if (!aligned16(w) || !aligned16(y) || (r > 0 && !aligned16(lora_b))) return RTL_ERR_MISALIGNED;
+  if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
+  const rtl_status d = check_device();
+  if (d != RTL_OK) return d;
+  return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y,
+                                          static_cast<hipStream_t>(hip_stream)));
+}
+
 RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const uint16_t* lora_a,
                                      const uint16_t* lora_b, int64_t M, int64_t N, int64_t K,
                                      int64_t r, float lora_scale, uint16_t* y, void* workspace,
@@ -89,18 +122,14 @@ RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const
   if (r > 0 && (lora_a == nullptr || lora_b == nullptr)) return RTL_ERR_NULL_POINTER;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return RTL_ERR_MISALIGNED;
   if (r > 0 && (!aligned16(lora_a) || !aligned16(lora_b))) return RTL_ERR_MISALIGNED;
-  const size_t need = rtl::ws_layout(M, K, r).total;
-  if (workspace == nullptr || workspace_bytes < need) return RTL_ERR_WORKSPACE;
+  if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
   const rtl_status d = check_device();
   if (d != RTL_OK) return d;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  const uint16_t* a = r > 0 ? lora_a : nullptr;
-  const uint16_t* b = r > 0 ? lora_b : nullptr;
-  hipError_t e = rtl::launch_prepass(x, a, M, K, r, lora_scale, workspace, stream);
-  if (e != hipSuccess) return RTL_ERR_HIP;
-  e = rtl::launch_sparse_gemm(workspace, w, b, M, N, K, r, y, stream);
-  return from_hip(e);
+  if (rtl::launch_prepass(x, r > 0 ? lora_a : nullptr, M, K, r, lora_scale, workspace, stream) != hipSuccess)
+    return RTL_ERR_HIP;
+  return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y, stream));
 }
 
 RTL_API rtl_status rtl_dense_linear(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,

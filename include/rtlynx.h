@@ -129,6 +129,33 @@ rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w,
                              void* hip_stream);
 
 /*
+ * rtl_sparse_linear_prepare / rtl_sparse_linear_apply - the two halves of
+ * rtl_sparse_linear, for callers that feed one activation to several weights
+ * (e.g. projections that share an input) or that time the halves apart.
+ *
+ * prepare reads x once: the 2:4 pattern decision, Top-K, norm-compensation
+ * scale, compression into the structured-sparse matrix-core operand order
+ * ("activation compression" and "layout generation", qingkeai article,
+ * section 04) and the LoRA-down product of the pruned residual (section
+ * 03.2), all written into `workspace`.  apply runs the sparse GEMM against w
+ * and the scale + LoRA-up epilogue, reading only the workspace, w and lora_b.
+ *
+ * Arguments mean what they mean for rtl_sparse_linear.  apply must see the
+ * same M, K and r as the prepare that filled the workspace, and the
+ * workspace must not be modified in between; apply may be called any number
+ * of times with different w / lora_b / N.  lora_scale is applied in prepare.
+ */
+rtl_status rtl_sparse_linear_prepare(const uint16_t* x, const uint16_t* lora_a,
+                                     int64_t M, int64_t K, int64_t r, float lora_scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* hip_stream);
+
+rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspace_bytes,
+                                   const uint16_t* w, const uint16_t* lora_b,
+                                   int64_t M, int64_t N, int64_t K, int64_t r,
+                                   uint16_t* y, void* hip_stream);
+
+/*
  * rtl_dense_linear - the dense baseline Y = X W^T (the denominator of the
  * speedups the pages quote, qingkeai article, section 05), bf16 inputs, fp32
  * accumulation on the dense matrix cores, bf16 output rounded to nearest even.

@@ -157,3 +157,38 @@ def test_python_wrappers_reject_bad_tensors():
     xb = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         rtl.dense_linear(xb, xb)          # host tensors
+
+
+def _pr(x=P, a=P2, m=64, k=256, r=8, alpha=1.0, ws=WSP, wsb=BIG, stream=None):
+    return rtl.lib().rtl_sparse_linear_prepare(x, a, m, k, r, alpha, ws, wsb, stream)
+
+
+def _ap(ws=WSP, wsb=BIG, w=P, b=P2, m=64, n=128, k=256, r=8, y=P3, stream=None):
+    return rtl.lib().rtl_sparse_linear_apply(ws, wsb, w, b, m, n, k, r, y, stream)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=6), SHAPE), (dict(r=129), SHAPE), (dict(m=-2), SHAPE),
+    (dict(x=None), NULLP), (dict(a=None), NULLP), (dict(x=P + 8), MISAL), (dict(a=P2 + 8), MISAL),
+    (dict(ws=None), WS), (dict(wsb=16), WS), (dict(ws=WSP + 4), MISAL), (dict(m=0), OK),
+])
+def test_prepare_rejects_invalid_arguments(kw, status):
+    assert _pr(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=6), SHAPE), (dict(n=-1), SHAPE), (dict(r=200), SHAPE),
+    (dict(w=None), NULLP), (dict(b=None), NULLP), (dict(y=None), NULLP),
+    (dict(w=P + 8), MISAL), (dict(b=P2 + 8), MISAL), (dict(y=P3 + 2), MISAL),
+    (dict(ws=None), WS), (dict(wsb=16), WS), (dict(m=0), OK), (dict(n=0), OK),
+])
+def test_apply_rejects_invalid_arguments(kw, status):
+    assert _ap(**kw) == status
+
+
+def test_prepare_apply_without_device():
+    if not _no_gpu():
+        pytest.skip("a GPU is present")
+    assert _pr() == NODEV
+    assert _ap() == NODEV
+    assert _pr(r=0, a=None) == NODEV

@@ -225,3 +225,20 @@ def test_full_size_config(name):
     assert_y_close(ys, oracle.sparse_linear_ref(x[rows], w, a, b), f"{name} sparse (sampled rows)")
     yds = y_to_f64(yd[torch.from_numpy(rows).to(DEV)])
     assert_y_close(yds, oracle.dense_linear_ref(x[rows], w), f"{name} dense (sampled rows)")
+
+
+def test_prepare_once_apply_many():
+    """One prepare feeding several weights (projections that share an input)
+    gives what separate sparse_linear calls give, bit for bit."""
+    rng = np.random.default_rng(31)
+    x = gen.mixture_bernoulli(rng, 384, 1024)
+    a = gen.gaussian_bits(rng, (64, 1024), 0.01)
+    xd, ad = to_dev(x), to_dev(a)
+    prep = rtl.prepare(xd, ad, 0.5)
+    for n in (256, 520, 1024):
+        w = gen.gaussian_bits(rng, (n, 1024), 0.02)
+        b = gen.gaussian_bits(rng, (n, 64), 0.01)
+        y1 = to_host(rtl.apply(prep, to_dev(w), to_dev(b)))
+        y2 = to_host(rtl.sparse_linear(xd, to_dev(w), ad, to_dev(b), lora_scale=0.5))
+        assert np.array_equal(y1, y2)
+        assert_y_close(oracle.bf16_bits_to_f64(y1), oracle.sparse_linear_ref(x, w, a, b, 0.5), f"apply N={n}")
