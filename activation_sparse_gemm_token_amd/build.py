@@ -29,6 +29,15 @@ COMMON = [
 ]
 
 
+# Per-source extra flags.  sparse_gemm: MFMA accumulators and operands in
+# the VGPR form -- with the default heuristic its 256-register accumulator
+# tile splits between VGPRs and AGPRs and the operand buffers spill to
+# scratch, whose reloads drain the load pipeline.
+EXTRA = {
+    "sparse_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -38,7 +47,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-x", "hip", "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l and l.strip())

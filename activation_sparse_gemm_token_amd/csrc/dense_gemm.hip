@@ -2,11 +2,17 @@
 // matrix cores (v_mfma_f32_16x16x32_bf16), fp32 accumulation, bf16 output.
 // This is the denominator of the speedups the RT-Lynx pages quote against
 // dense GEMM (qingkeai article, section 05).  It shares the tiling, the W
-// staging and the tile order of the structured-sparse kernel so that the two
-// differ only in the A operand and the matrix instruction.
+// ring in LDS, the step structure and the tile order of the structured-
+// sparse kernel, so that the two differ only in the A operand and the
+// matrix instruction.
 //
-// A fragments come straight from X in global memory: lane l takes token
-// m0 + l % 16 and channels k + 8 (l / 16) + [0, 8), one 16-byte load.
+// The A tile (256 tokens x 64 channels of X per step) goes through LDS in
+// the same operand order as W -- for each 16-token block and 32-channel
+// half, 64 lanes x 16 bytes, lane l holding token l % 16, channels
+// 8 (l / 16) + [0, 8) -- copied by the same DMA routine, in a 2-stage ring
+// next to the 3-stage W ring (96 + 64 KiB of LDS).
+#include <type_traits>
+
 #include "gemm_common.hpp"
 #include "rtl_kernels.hpp"
 
@@ -14,34 +20,21 @@ namespace rtl {
 
 namespace {
 
-template <bool ALIGNED16>
-__device__ __forceinline__ u32x4 load_a_dense(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                              int64_t m, int64_t k) {
-  u32x4 v = (u32x4){0, 0, 0, 0};
-  if (m < M) {
-    const uint16_t* p = x + m * K + k;
-    if constexpr (ALIGNED16) {
-      if (k + 8 <= K) v = *reinterpret_cast<const u32x4*>(p);
-    } else {
-      if (k + 4 <= K) { const u32x2 a = *reinterpret_cast<const u32x2*>(p); v[0] = a[0]; v[1] = a[1]; }
-      if (k + 8 <= K) { const u32x2 b = *reinterpret_cast<const u32x2*>(p + 4); v[2] = b[0]; v[3] = b[1]; }
-    }
-  }
-  return v;
-}
-
-template <bool ALIGNED16>
+template <int KM>
 __global__ void __launch_bounds__(kGemmThreads, 1)
 dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                   int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) char lds[2][kWTileBytes];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWStages = 3, kAStages = 2;
+  __shared__ __attribute__((aligned(16))) char lds_w[kWStages][kWTileBytes];
+  __shared__ __attribute__((aligned(16))) char lds_a[kAStages][kWTileBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (N + kTileN - 1) / kTileN;
   int64_t tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
   const int64_t n0 = tn * kTileN;
-  const int64_t m0 = tm * kTileM + wm * kWaveM;
+  const int64_t m0 = tm * kTileM;
   const int64_t ksteps = (K + kTileK - 1) / kTileK;
 
   f32x4 acc[kRB][kCB];
@@ -50,48 +43,96 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
 #pragma unroll
     for (int j = 0; j < kCB; ++j) acc[i][j] = (f32x4){0, 0, 0, 0};
 
-  u32x4 a_cur[2][kRB], a_nxt[2][kRB];
-  auto load_a = [&](int64_t ks, u32x4 (&a)[2][kRB]) {
+  // Rows past M / N lie past the end of X / W and read as zeros; channels
+  // past K are pointed out of range in the tail modes.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, M * K * 2);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, N * K * 2);
+  const WTileOffsets xo = w_tile_offsets(K, m0);
+  const WTileOffsets wo = w_tile_offsets(K, n0);
+  const char* b_base = &lds_w[0][0] + 16 * lane + wn * kCB * 2048;
+  const char* a_base = &lds_a[0][0] + 16 * lane + wm * kRB * 2048;
+  constexpr int kTileOps = KM == kAligned8 ? 4 * kWChunksPerThread : kWChunksPerThread;
+
+  // Both tile copies are issued as inline-asm DMA blocks: no vector-memory
+  // operation of the loop is visible to the compiler, so it inserts no
+  // vmcnt waits of its own (it cannot always prove that a copy into one
+  // stage does not alias the reads of another) and the explicit waits below
+  // are exact.  The K % 8 == 4 mode uses the compiler-visible dword copy.
+  auto copy_tile = [&](__amdgpu_buffer_rsrc_t rs, const WTileOffsets& o, int64_t row0, int64_t rows,
+                       int64_t ks, char* dst) {
+    if constexpr (KM == kAligned8) {
+      dma_w_tile_dword(rs, rows, K, row0, ks * kTileK, dst);
+    } else {
+      const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(dst);
+      dma_w_tile_asm(rs, o, K, ks * kTileK, lds_addr, KM == kAligned16);
+    }
+  };
+
+  // Step ks: W stage ks % 3, A stage ks % 2.  Each step issues the A copy
+  // of step ks + 1, then the W copy of step ks + 2, so at its top only the
+  // W copy of step ks + 1 may still be in flight.
+  auto step = [&](int64_t ks, auto bw_c, auto ba_c) {
+    constexpr int bw = decltype(bw_c)::value;
+    constexpr int ba = decltype(ba_c)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<kTileOps>();
+    barrier_no_fence();
+    const int64_t ka = ks + 1 < ksteps ? ks + 1 : ksteps - 1;
+    const int64_t kw = ks + 2 < ksteps ? ks + 2 : ksteps - 1;
+    copy_tile(xr, xo, m0, M, ka, lds_a[1 - ba]);
+    copy_tile(wr, wo, n0, N, kw, lds_w[(bw + 2) % kWStages]);
+    __builtin_amdgcn_sched_barrier(0);
+    const char* bs = b_base + bw * kWTileBytes;
+    const char* as = a_base + ba * kWTileBytes;
+    bf16x8 af[2][kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        a[h][rb] = load_a_dense<ALIGNED16>(x, M, K, m0 + 16 * rb + (lane & 15),
-                                           ks * kTileK + 32 * h + 8 * (lane >> 4));
-  };
-
-  WTileLoader<ALIGNED16> wl;
-  wl.issue(w, N, K, n0, 0, lds[0]);
-  wl.commit(lds[0]);
-  load_a(0, a_cur);
-
-  for (int64_t ks = 0; ks < ksteps; ++ks) {
-    wait_vm_all();
-    __syncthreads();
-    const bool more = ks + 1 < ksteps;
-    if (more) {
-      wl.issue(w, N, K, n0, (ks + 1) * kTileK, lds[(ks + 1) & 1]);
-      load_a(ks + 1, a_nxt);
-    }
-    const char* stage = lds[ks & 1];
+        af[h][rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + rb * 2048 + h * 1024));
+    u32x4 q0 = *reinterpret_cast<const u32x4*>(bs);
+    u32x4 q1 = *reinterpret_cast<const u32x4*>(bs + 1024);
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
-      const int gcb = wn * kCB + cb;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + (2 * gcb + h) * 1024 + 16 * lane));
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a_cur[h][rb]), b, acc[rb][cb], 0, 0, 0);
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, q0), b1 = __builtin_bit_cast(bf16x8, q1);
+      if (cb + 1 < kCB) {
+        q0 = *reinterpret_cast<const u32x4*>(bs + (cb + 1) * 2048);
+        q1 = *reinterpret_cast<const u32x4*>(bs + (cb + 1) * 2048 + 1024);
       }
-    }
-    if (more) {
-      wl.commit(lds[(ks + 1) & 1]);
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) { a_cur[0][rb] = a_nxt[0][rb]; a_cur[1][rb] = a_nxt[1][rb]; }
+      for (int rb = 0; rb < kRB; ++rb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0][rb], b0, acc[rb][cb], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1][rb], b1, acc[rb][cb], 0, 0, 0);
     }
+  };
+
+  copy_tile(wr, wo, n0, N, 0, lds_w[0]);
+  copy_tile(xr, xo, m0, M, 0, lds_a[0]);
+  copy_tile(wr, wo, n0, N, ksteps > 1 ? 1 : 0, lds_w[1]);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  int64_t ks = 0;
+  for (; ks + 6 <= ksteps; ks += 6) {
+    step(ks + 0, I0{}, I0{});
+    step(ks + 1, I1{}, I1{});
+    step(ks + 2, I2{}, I0{});
+    step(ks + 3, I0{}, I1{});
+    step(ks + 4, I1{}, I0{});
+    step(ks + 5, I2{}, I1{});
   }
-  store_acc_bf16(acc, y, M, N, m0, n0 + wn * kWaveN);
+  // 0 to 5 steps left (K need not be a multiple of 384).
+  if (ks < ksteps) step(ks + 0, I0{}, I0{});
+  if (ks + 1 < ksteps) step(ks + 1, I1{}, I1{});
+  if (ks + 2 < ksteps) step(ks + 2, I2{}, I0{});
+  if (ks + 3 < ksteps) step(ks + 3, I0{}, I1{});
+  if (ks + 4 < ksteps) step(ks + 4, I1{}, I0{});
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<0>();
+
+  store_acc_bf16(acc, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
 }
 
 }  // namespace
@@ -100,8 +141,9 @@ hipError_t launch_dense_gemm(const uint16_t* x, const uint16_t* w, int64_t M, in
                              int64_t K, uint16_t* y, hipStream_t stream) {
   const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
   const dim3 grid((unsigned)tiles), block(kGemmThreads);
-  if (K % 8 == 0) dense_gemm_kernel<true><<<grid, block, 0, stream>>>(x, w, M, N, K, y);
-  else dense_gemm_kernel<false><<<grid, block, 0, stream>>>(x, w, M, N, K, y);
+  if (K % kTileK == 0) dense_gemm_kernel<kFullK><<<grid, block, 0, stream>>>(x, w, M, N, K, y);
+  else if (K % 8 == 0) dense_gemm_kernel<kAligned16><<<grid, block, 0, stream>>>(x, w, M, N, K, y);
+  else dense_gemm_kernel<kAligned8><<<grid, block, 0, stream>>>(x, w, M, N, K, y);
   return hipGetLastError();
 }
 

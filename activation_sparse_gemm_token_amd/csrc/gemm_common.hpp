@@ -24,54 +24,190 @@ constexpr int kWChunksPerThread = kWTileBytes / 16 / kGemmThreads;   // 8
 
 // W-tile copy.  Thread (wave v, lane l) moves chunk i: 16-column block
 // cb = 4 v + i / 2, half h = i % 2, column n0 + 16 cb + l % 16, channels
-// k0 + 32 h + 8 (l / 16) + [0, 8), to LDS byte offset (2 cb + h) * 1024 + 16 l.
-// Columns past N read row N - 1 (their results are never stored).  Channels
-// past K read channel 0 of the same row: finite values that meet zeros in
-// the A operand.
+// k0 + 32 h + 8 (l / 16) + [0, 8), to LDS byte offset (2 cb + h) * 1024 + 16 l,
+// so every LDS write and read is lane-contiguous.  Columns past N read row
+// N - 1 (their results are never stored); channels past K read as zero.
 //
-// With 16-byte aligned rows (K % 8 == 0) the copy is a direct global -> LDS
-// load (global_load_lds_dwordx4), which writes lane l's 16 bytes to
-// base + 16 l and needs no registers; the caller waits on vmcnt before the
-// barrier that publishes the stage.  Otherwise rows are 8-byte aligned and the
-// copy goes through registers in 8-byte halves.
-__device__ __forceinline__ const uint16_t* w_chunk_ptr(const uint16_t* __restrict__ w, int64_t N, int64_t K,
-                                                       int64_t n0, int64_t k0, int i, int64_t& k) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cb = 4 * wave + i / 2, h = i % 2;
-  int64_t n = n0 + 16 * cb + (lane & 15);
-  n = n < N ? n : N - 1;
-  k = k0 + 32 * h + 8 * (lane >> 4);
-  return w + n * K;
+// The copy goes through registers: the global loads of step k+1 are issued
+// at the top of step k and written to LDS at its end, so the compiler's own
+// vmcnt tracking waits exactly for them.  (The direct global->LDS form makes
+// the compiler drain every outstanding load before the next LDS read, which
+// serialises a memory latency into each step.)
+// Buffer resource over a whole tensor (raw, stride 0): loads past
+// `bytes` return zeros instead of faulting.  Tensors hold fewer than 2^31
+// elements, so byte offsets fit the 32-bit offset fields.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void load_w_tile_direct(const uint16_t* __restrict__ w, int64_t N, int64_t K,
-                                                   int64_t n0, int64_t k0, char* lds_stage) {
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// How channel tails are handled.  kFullK: every k-step lies inside K (no
+// guard, the common case); kAligned16: rows are 16-byte aligned and the last
+// k-step is partial (16-byte loads, guarded per chunk); kAligned8: K % 8 == 4,
+// rows are only 8-byte aligned (8-byte loads, guarded per group).
+enum KMode { kFullK = 0, kAligned16 = 1, kAligned8 = 2 };
+
+// Byte offsets (at channel 0) of the thread's 8 chunks of a W tile: one
+// per-lane base (row n0 + 64 wave + l % 16, channel 8 (l / 16)) plus a
+// uniform per-chunk step (16 (i / 2) rows, 32 (i % 2) channels), so only one
+// VGPR stays live.  Rows past N lie past the end of W and read as zeros
+// (the row is in the VGPR offset, which the buffer range check covers).
+struct WTileOffsets {
+  uint32_t base;                  // VGPR
+  uint32_t row16;                 // uniform: bytes of 16 rows
+  int32_t k_lane;                 // 8 (l / 16)
+  __device__ __forceinline__ uint32_t off(int i) const {
+    return base + (uint32_t)(i / 2) * row16 + (uint32_t)(i % 2) * 64u;
+  }
+};
+
+__device__ __forceinline__ WTileOffsets w_tile_offsets(int64_t K, int64_t n0) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  WTileOffsets o;
+  o.k_lane = 8 * (lane >> 4);
+  o.base = (uint32_t)(((n0 + 64 * wave + (lane & 15)) * K + o.k_lane) * 2);
+  o.row16 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * K * 2));
+  return o;
+}
+
+// Byte offset that lies past every tensor: a buffer load there returns zeros.
+constexpr uint32_t kOobOffset = 0xfffffff0u;
+
+// Direct global -> LDS copy of the W tile at channel k0 (K % 8 == 0): each
+// buffer_load_dwordx4 ... lds writes lane l's 16 bytes to base + 16 l, so
+// chunk i of every lane lands at (2 cb + h) * 1024 + 16 l without touching
+// registers.  Chunks past K are pointed out of the buffer and arrive as
+// zeros.  The caller waits on vmcnt before the barrier that publishes them.
+template <bool GUARD_K>
+__device__ __forceinline__ void dma_w_tile(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
+                                           int64_t k0, char* lds_stage) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t soff = (uint32_t)(k0 * 2);
 #pragma unroll
   for (int i = 0; i < kWChunksPerThread; ++i) {
-    int64_t k;
-    const uint16_t* row = w_chunk_ptr(w, N, K, n0, k0, i, k);
-    const uint16_t* src = row + (k + 8 <= K ? k : 0);
+    uint32_t voff = o.off(i);
+    if constexpr (GUARD_K) {
+      const int64_t k = k0 + 32 * (i % 2) + o.k_lane;
+      voff = (k + 8 <= K) ? voff : kOobOffset - soff;
+    }
     char* dst = lds_stage + (2 * (4 * wave + i / 2) + i % 2) * 1024;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(dst), 16, voff, soff, 0, 0);
   }
 }
 
-__device__ __forceinline__ void load_w_tile_regs(const uint16_t* __restrict__ w, int64_t N, int64_t K,
-                                                 int64_t n0, int64_t k0, u32x4 (&st)[kWChunksPerThread]) {
+// The same copy issued as one inline-asm block of 8 buffer_load_dwordx4 ...
+// lds instructions.  The compiler does not see these loads, so it never
+// inserts vmcnt waits for them (with the builtin it sometimes cannot prove
+// that a copy into one stage does not alias reads of another, and drains
+// all loads); the caller accounts for them with explicit vmcnt waits.  The
+// block has no output registers -- the data goes to LDS -- and writes only
+// M0, which it saves and restores; it uses no instruction that sets SCC.
+// s_nop 4 covers a VALU write of an SGPR operand right before the block.
+__device__ __forceinline__ void dma_w_tile_asm(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
+                                               int64_t k0, uint32_t lds_stage_addr, bool guard_k) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(k0 * 2));
+  uint32_t v[kWChunksPerThread];
 #pragma unroll
   for (int i = 0; i < kWChunksPerThread; ++i) {
-    int64_t k;
-    const uint16_t* p = w_chunk_ptr(w, N, K, n0, k0, i, k) + k;
+    v[i] = o.off(i);
+    if (guard_k) {
+      const int64_t k = k0 + 32 * (i % 2) + o.k_lane;
+      v[i] = (k + 8 <= K) ? v[i] : kOobOffset - soff;
+    }
+  }
+  // LDS byte address of chunk i: stage + (2 (4 wave + i / 2) + i % 2) * 1024
+  // = stage + 8192 wave + 1024 i.  All eight are computed outside the block,
+  // which then only moves them into M0 (s_mov does not touch SCC).
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_stage_addr + 8192u * (uint32_t)wave);
+  uint32_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[l0]\n\t"
+      "buffer_load_dwordx4 %[v0], %[rs], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[l1]\n\t"
+      "buffer_load_dwordx4 %[v1], %[rs], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[l2]\n\t"
+      "buffer_load_dwordx4 %[v2], %[rs], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[l3]\n\t"
+      "buffer_load_dwordx4 %[v3], %[rs], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[l4]\n\t"
+      "buffer_load_dwordx4 %[v4], %[rs], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[l5]\n\t"
+      "buffer_load_dwordx4 %[v5], %[rs], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[l6]\n\t"
+      "buffer_load_dwordx4 %[v6], %[rs], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[l7]\n\t"
+      "buffer_load_dwordx4 %[v7], %[rs], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [v4] "v"(v[4]), [v5] "v"(v[5]),
+        [v6] "v"(v[6]), [v7] "v"(v[7]), [rs] "s"(wr), [so] "s"(soff), [l0] "s"(l0), [l1] "s"(l0 + 0x400u),
+        [l2] "s"(l0 + 0x800u), [l3] "s"(l0 + 0xc00u), [l4] "s"(l0 + 0x1000u), [l5] "s"(l0 + 0x1400u),
+        [l6] "s"(l0 + 0x1800u), [l7] "s"(l0 + 0x1c00u)
+      : "memory");
+  (void)saved;
+}
+
+// W-tile copy for K % 8 == 4 (rows only 8-byte aligned): 32 dword DMAs per
+// thread through the builtin, which the compiler tracks (and drains before
+// later LDS reads -- slow, but this mode only serves odd channel counts).
+// DMA lane j of instruction (b, q) carries dword j % 4 of the chunk of lane
+// 16 q + j / 4 in chunk block b, so the LDS layout matches the 16-byte copy.
+__device__ __forceinline__ void dma_w_tile_dword(__amdgpu_buffer_rsrc_t wr, int64_t N, int64_t K, int64_t n0,
+                                                 int64_t k0, char* lds_stage) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int b = 0; b < kWChunksPerThread; ++b) {
+    const int cb = 4 * wave + b / 2, h = b % 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = n0 + 16 * cb + (lane >> 2);
+      const int64_t k = k0 + 32 * h + 8 * q + 2 * (lane & 3);
+      const uint32_t voff = (k + 2 <= K && n < N) ? (uint32_t)((n * K + k) * 2) : kOobOffset;
+      char* dst = lds_stage + (2 * cb + h) * 1024 + 256 * q;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(dst), 4, voff, 0, 0, 0);
+    }
+  }
+}
+
+// Workgroup barrier without the release fence of __syncthreads(), whose
+// "vmcnt(0)" would also drain the W copies of later stages still in flight.
+// The asm statement is a full compiler memory barrier; the caller waits
+// explicitly for the data the barrier publishes.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// Waits until at most n vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Register copy of the W tile for K % 8 == 4 (rows only 8-byte aligned).
+__device__ __forceinline__ void load_w_tile_8(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
+                                              int64_t k0, u32x4 (&st)[kWChunksPerThread]) {
+  const uint32_t soff = (uint32_t)(k0 * 2);
+#pragma unroll
+  for (int i = 0; i < kWChunksPerThread; ++i) {
+    const int64_t k = k0 + 32 * (i % 2) + o.k_lane;
     u32x4 v = (u32x4){0, 0, 0, 0};
-    if (k + 4 <= K) { const u32x2 a = *reinterpret_cast<const u32x2*>(p); v[0] = a[0]; v[1] = a[1]; }
-    if (k + 8 <= K) { const u32x2 b = *reinterpret_cast<const u32x2*>(p + 4); v[2] = b[0]; v[3] = b[1]; }
+    if (k + 4 <= K) { const u32x2 a = buf_load8(wr, o.off(i), soff); v[0] = a[0]; v[1] = a[1]; }
+    if (k + 8 <= K) { const u32x2 b = buf_load8(wr, o.off(i) + 8, soff); v[2] = b[0]; v[3] = b[1]; }
     st[i] = v;
   }
 }
 
 __device__ __forceinline__ void store_w_tile(char* lds_stage, const u32x4 (&st)[kWChunksPerThread]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int i = 0; i < kWChunksPerThread; ++i) {
     const int cb = 4 * wave + i / 2, h = i % 2;
@@ -79,37 +215,45 @@ __device__ __forceinline__ void store_w_tile(char* lds_stage, const u32x4 (&st)[
   }
 }
 
-// Issues the copy of one W tile into an LDS stage.  In the register path the
-// LDS write is deferred to commit_w_tile so that the global loads overlap the
-// matrix work of the current stage.
-template <bool ALIGNED16>
-struct WTileLoader {
-  u32x4 st[ALIGNED16 ? 1 : kWChunksPerThread];
-  __device__ __forceinline__ void issue(const uint16_t* __restrict__ w, int64_t N, int64_t K,
-                                        int64_t n0, int64_t k0, char* lds_stage) {
-    if constexpr (ALIGNED16) load_w_tile_direct(w, N, K, n0, k0, lds_stage);
-    else load_w_tile_regs(w, N, K, n0, k0, st);
-  }
-  __device__ __forceinline__ void commit(char* lds_stage) {
-    if constexpr (!ALIGNED16) store_w_tile(lds_stage, st);
-  }
-};
+// Starts the copy of the W tile of channel k0 into an LDS stage.  DMA modes
+// finish on their own (vmcnt); the register mode holds the data in `st`
+// until commit_w_tile writes it.
+template <int KM, int NS>
+__device__ __forceinline__ void issue_w_tile(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
+                                             int64_t k0, char* lds_stage, u32x4 (&st)[NS]) {
+  if constexpr (KM == kAligned8) load_w_tile_8(wr, o, K, k0, st);
+  else dma_w_tile<KM == kAligned16>(wr, o, K, k0, lds_stage);
+}
+
+template <int KM, int NS>
+__device__ __forceinline__ void commit_w_tile(char* lds_stage, const u32x4 (&st)[NS]) {
+  if constexpr (KM == kAligned8) store_w_tile(lds_stage, st);
+}
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Tile order: tiles are taken in column panels of kGroupM tile rows so that
-// workgroups running together share W panels in L2.
-constexpr int kGroupM = 8;
+// Tile order.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup id i runs on XCD i % 8), and each XCD has its own L2.  The id
+// is first renumbered so that every XCD owns a contiguous range of tiles,
+// then that range is walked in groups of kGroupN tile columns, column
+// fastest, so the ~32 tiles an XCD runs at once form an 8 x 4 block: per
+// k-step they share 8 A slices and 4 W slices in L2 instead of 1 and 32.
+constexpr int kXcds = 8;
+constexpr int kGroupN = 4;
 
 __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  const int64_t total = tiles_m * tiles_n;
   const int64_t id = blockIdx.x;
-  const int64_t per_group = (int64_t)kGroupM * tiles_n;
-  const int64_t g = id / per_group;
-  const int64_t first_m = g * kGroupM;
-  const int64_t gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
-  const int64_t in = id - g * per_group;
-  tm = first_m + in % gm;
-  tn = in / gm;
+  const int64_t xcd = id % kXcds, local = id / kXcds;
+  const int64_t per = total / kXcds, extra = total % kXcds;
+  const int64_t lin = xcd * per + (xcd < extra ? xcd : extra) + local;   // bijection on [0, total)
+  const int64_t per_group = (int64_t)kGroupN * tiles_m;
+  const int64_t g = lin / per_group;
+  const int64_t first_n = g * kGroupN;
+  const int64_t gw = tiles_n - first_n < kGroupN ? tiles_n - first_n : kGroupN;
+  const int64_t in = lin - g * per_group;
+  tm = in / gw;
+  tn = first_n + in % gw;
 }
 
 // Stores a wavefront's 128 x 128 fp32 accumulators as bf16.

@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--workload", default="mlp_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--counters", action="store_true",
+                    help="a short launch sequence for rocprofv3 --pmc passes: 3 x (prepare, apply, dense, "
+                         "sparsify) and 3 plain 256 MiB copies (the calibration kernel); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer runs on a single MI355X; "
@@ -119,6 +122,22 @@ def main():
     def step():
         p = rtl.prepare(xd, ad, 1.0, workspace=ws)
         rtl.apply(p, wd, bd, out=y)
+
+    if args.counters:
+        src = torch.empty((256 << 20,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        vals = torch.empty((m, k // 2), dtype=torch.bfloat16, device=dev)
+        idx = torch.empty((m, (k // 4 + 1) // 2), dtype=torch.uint8, device=dev)
+        scale = torch.empty((m,), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            step()
+            rtl.dense_linear(xd, wd, out=y)
+            rtl.sparsify_2of4(xd)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] counter sequence done")
+        return
 
     for _ in range(args.warmup):
         step()
