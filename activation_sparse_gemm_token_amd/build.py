@@ -31,8 +31,8 @@ COMMON = [
 
 # Per-source extra flags.  sparse_gemm: MFMA accumulators and operands in
 # the VGPR form -- with the default heuristic its 256-register accumulator
-# tile splits between VGPRs and AGPRs and the operand buffers spill to
-# scratch, whose reloads drain the load pipeline.
+# tile splits between VGPRs and AGPRs and values spill to scratch, whose
+# reloads (vector-memory operations) would drain the DMA pipeline.
 EXTRA = {
     "sparse_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }

@@ -274,4 +274,50 @@ __device__ __forceinline__ void store_acc_bf16(const f32x4 (&acc)[kRB][kCB], uin
   }
 }
 
+// Epilogue store through LDS.  Each wavefront writes its 128 x 128 tile
+// as bf16 into its own LDS region (row pitch 288 bytes: the 32-byte row
+// segments of the 4 row groups of one write land on distinct banks), then
+// reads it back 16 bytes per lane along rows and issues 32 coalesced 16-byte
+// buffer stores (4 rows of 256 bytes each) instead of 256 scattered 2-byte
+// stores.  The caller must have drained every DMA and passed a barrier, so
+// that the LDS ring is free (needs 4 x 36 KiB).  Rows past M lie past the
+// end of Y and are dropped by the buffer range check; column chunks past N
+// are pointed out of range (N % 8 == 0 is required: a chunk is all in or
+// all out).
+constexpr int kStorePitch = 288;
+constexpr int kStoreRegion = kWaveM * kStorePitch;      // 36 KiB per wavefront
+
+__device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[kRB][kCB], char* lds_base,
+                                                   uint16_t* __restrict__ y, int64_t M, int64_t N,
+                                                   int64_t m0, int64_t n0) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  char* region = lds_base + wave * kStoreRegion;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * rb + 4 * (lane >> 4) + i, col = 16 * cb + (lane & 15);
+        *reinterpret_cast<uint16_t*>(region + row * kStorePitch + 2 * col) =
+            (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
+      }
+  // Only this wavefront reads its region back: a wave-local LDS wait suffices.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, M * N * 2);
+  const int sub_row = lane >> 4, chunk = lane & 15;        // 4 rows x 16 chunks of 8 columns
+  const int64_t col = n0 + 8 * chunk;
+  const bool col_ok = col + 8 <= N;
+  const uint32_t lane_off = (uint32_t)(((m0 + sub_row) * N + col) * 2);
+  const uint32_t row4 = __builtin_amdgcn_readfirstlane((uint32_t)(4 * N * 2));
+#pragma unroll
+  for (int it = 0; it < kWaveM / 4; ++it) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region + (4 * it + sub_row) * kStorePitch + 16 * chunk);
+    const uint32_t soff = (uint32_t)it * row4;
+    const uint32_t voff = col_ok ? lane_off : kOobOffset - soff;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), yr,
+                                           voff, soff, 0);
+  }
+}
+
 }  // namespace rtl

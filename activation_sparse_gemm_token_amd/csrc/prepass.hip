@@ -119,7 +119,7 @@ template <bool ALIGNED16, int NCB>
 __global__ void __launch_bounds__(64 * kWaves)
 prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora_a,
                int64_t M, int64_t K, int64_t r, float alpha,
-               u32x4* __restrict__ xv, uint32_t* __restrict__ xi, float* __restrict__ s_out,
+               u32x4* __restrict__ xv, uint16_t* __restrict__ xi, float* __restrict__ s_out,
                u32x4* __restrict__ t_out, int64_t kpairs, int64_t rsteps) {
   // NCB = 16-wide column blocks of the LoRA rank covered (0: no LoRA branch).
   constexpr int NT = NCB > 0 ? NCB : 1;
@@ -153,7 +153,8 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
     const int64_t grp = mb >> 3, sub = mb & 7;
     xv[((grp * ksteps + ks0) * 8 + sub) * 64 + lane] = q0.kept;
     xv[((grp * ksteps + ks0 + 1) * 8 + sub) * 64 + lane] = q1.kept;
-    xi[((grp * kpairs + p) * 8 + sub) * 64 + lane] = q0.kcode | (q1.kcode << 16);
+    xi[((grp * ksteps + ks0) * 64 + lane) * 8 + sub] = (uint16_t)q0.kcode;
+    xi[((grp * ksteps + ks0 + 1) * 64 + lane) * 8 + sub] = (uint16_t)q1.kcode;
     if constexpr (NCB > 0) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
@@ -230,7 +231,7 @@ hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M
                             int64_t r, float alpha, const WsLayout& L, char* ws, hipStream_t stream) {
   const dim3 grid((unsigned)(L.mp / 16)), block(64 * kWaves);
   u32x4* xv = reinterpret_cast<u32x4*>(ws + L.off_xv);
-  uint32_t* xi = reinterpret_cast<uint32_t*>(ws + L.off_xi);
+  uint16_t* xi = reinterpret_cast<uint16_t*>(ws + L.off_xi);
   float* s = reinterpret_cast<float*>(ws + L.off_s);
   u32x4* t = reinterpret_cast<u32x4*>(ws + L.off_t);
   const int64_t kpairs = L.kp / 128, rsteps = L.rp / 32;

@@ -23,7 +23,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 //   xv: compressed values, 16-token blocks mb grouped in eights:
 //       [mb / 8][k-step][mb % 8][lane] x 16 bytes, so the 8 fragments one
 //       wavefront needs for a k-step are 8 KiB contiguous;
-//   xi: 2-bit positions, [mb / 8][k-pair][mb % 8][lane] x 4 bytes;
+//   xi: 2-bit positions, 16 bits per lane and k-step (the lane's four
+//       groups), [mb / 8][k-step][lane][mb % 8] x 2 bytes, so one 16-byte
+//       read gives a lane the fields of all 8 row blocks;
 //   s:  per-token scale, fp32 [mp];
 //   t:  alpha * T as bf16 hi and lo, [mb][r-step][hi, lo][lane] x 16 bytes.
 // ---------------------------------------------------------------------------
@@ -42,7 +44,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t M, int64_t K, int64_t r) {
   size_t o = 0;
   L.off_xv = o; o += (size_t)L.mp * (size_t)L.kp;                 // (mp/16)(kp/64) x 1 KiB
   o = (size_t)round_up((int64_t)o, 256);
-  L.off_xi = o; o += (size_t)L.mp * (size_t)L.kp / 8;             // (mp/16)(kp/128) x 64 lanes x 4 B
+  L.off_xi = o; o += (size_t)L.mp * (size_t)L.kp / 8;             // (mp/128)(kp/64) x 64 lanes x 8 x 2 B
   o = (size_t)round_up((int64_t)o, 256);
   L.off_s = o; o += (size_t)L.mp * 4;
   o = (size_t)round_up((int64_t)o, 256);

@@ -21,15 +21,71 @@ namespace rtl {
 
 namespace {
 
+// Per k-step LDS stage: the W tile (32 KiB), the workgroup's 256 rows of
+// compressed A (16 x 1 KiB fragments) and their position fields (2 x 1 KiB).
+constexpr int kAStageOff = kWTileBytes;
+constexpr int kIStageOff = kWTileBytes + 16 * 1024;
+constexpr int kStageBytes = kWTileBytes + 18 * 1024;
+
+// Copies the compressed A operand of one k-step into an LDS stage: thread
+// (wave v, i) moves fragment c = 4 v + i (16-token block c % 8 of group
+// c / 8) with one buffer_load_dwordx4 ... lds, and 256 bytes of the position
+// fields with each of two buffer_load_dword ... lds (parts 2v, 2v + 1 of the
+// two groups' 2 KiB).  Same rules as dma_w_tile_asm: no output registers,
+// M0 saved and restored, no SCC write.  6 vector-memory operations.
+__device__ __forceinline__ void dma_a_tile_asm(__amdgpu_buffer_rsrc_t ar, __amdgpu_buffer_rsrc_t ir,
+                                               uint32_t a_group0, uint32_t i_group0, uint32_t a_gstride,
+                                               uint32_t i_gstride, int64_t ks, uint32_t lds_stage_addr) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // fragments 4v .. 4v+3 all lie in group v / 2, blocks 4 (v % 2) .. +3
+  const uint32_t g = wave >> 1;
+  const uint32_t a_so = __builtin_amdgcn_readfirstlane(a_group0 + g * a_gstride + (uint32_t)ks * 8192u +
+                                                       (wave & 1u) * 4096u);
+  const uint32_t la = __builtin_amdgcn_readfirstlane(lds_stage_addr + kAStageOff + wave * 4096u);
+  // position parts 2v, 2v+1: group v / 2, bytes 512 (v % 2) .. +512
+  const uint32_t i_so = __builtin_amdgcn_readfirstlane(i_group0 + g * i_gstride + (uint32_t)ks * 1024u +
+                                                       (wave & 1u) * 512u);
+  const uint32_t li = __builtin_amdgcn_readfirstlane(lds_stage_addr + kIStageOff + wave * 512u);
+  const uint32_t va = 16u * lane, vi = 4u * lane;
+  uint32_t saved;
+  // The instruction offset of a buffer ... lds load is added to the LDS
+  // address too, so every offset is carried by the scalar offset operand.
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[la0]\n\t"
+      "buffer_load_dwordx4 %[va], %[ar], %[aso0] offen lds\n\t"
+      "s_mov_b32 m0, %[la1]\n\t"
+      "buffer_load_dwordx4 %[va], %[ar], %[aso1] offen lds\n\t"
+      "s_mov_b32 m0, %[la2]\n\t"
+      "buffer_load_dwordx4 %[va], %[ar], %[aso2] offen lds\n\t"
+      "s_mov_b32 m0, %[la3]\n\t"
+      "buffer_load_dwordx4 %[va], %[ar], %[aso3] offen lds\n\t"
+      "s_mov_b32 m0, %[li0]\n\t"
+      "buffer_load_dword %[vi], %[ir], %[iso0] offen lds\n\t"
+      "s_mov_b32 m0, %[li1]\n\t"
+      "buffer_load_dword %[vi], %[ir], %[iso1] offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [va] "v"(va), [vi] "v"(vi), [ar] "s"(ar), [ir] "s"(ir),
+        [aso0] "s"(a_so), [aso1] "s"(a_so + 1024u), [aso2] "s"(a_so + 2048u), [aso3] "s"(a_so + 3072u),
+        [iso0] "s"(i_so), [iso1] "s"(i_so + 256u),
+        [la0] "s"(la), [la1] "s"(la + 1024u), [la2] "s"(la + 2048u), [la3] "s"(la + 3072u),
+        [li0] "s"(li), [li1] "s"(li + 256u)
+      : "memory");
+  (void)saved;
+}
+
 template <int KM>
 __global__ void __launch_bounds__(kGemmThreads, 1)
-sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint32_t* __restrict__ xi,
+sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi,
                    const float* __restrict__ s, const u32x4* __restrict__ tfrag,
                    const uint16_t* __restrict__ w, const uint16_t* __restrict__ lora_b,
                    int64_t M, int64_t N, int64_t K, int64_t r, int64_t kpairs,
                    int64_t rsteps, uint16_t* __restrict__ y) {
-  constexpr int kStages = 3;                                   // W ring in LDS, prefetch distance 2
-  __shared__ __attribute__((aligned(16))) char lds[kStages][kWTileBytes];
+  constexpr int kStages = 3;                                   // LDS ring, prefetch distance 2
+  __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
   const int wm = wave >> 1, wn = wave & 1;
@@ -46,64 +102,54 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint32_t* __restrict__ xi
 #pragma unroll
     for (int j = 0; j < kCB; ++j) acc[i][j] = (f32x4){0, 0, 0, 0};
 
-  // A fragments and index words: two step buffers, filled one step ahead
-  // (W runs two steps ahead through the LDS ring).  The workspace keeps the
-  // wavefront's 8 row blocks of one k-step in 8 KiB of contiguous memory.
-  // Prefetches past the last step re-read the last step (no branch in the
-  // loop; the data is never used).
+  // Every operand of the main loop arrives by DMA into a 3-stage LDS ring,
+  // two k-steps ahead; nothing in the loop is a compiler-visible memory
+  // load, so the explicit vmcnt waits are exact.
   const int64_t mgroups = (tiles_m * kTileM) / 128;      // 8-block groups in the workspace
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(xv, mgroups * ksteps * 8 * 1024);
-  const __amdgpu_buffer_rsrc_t ir = make_rsrc(xi, mgroups * kpairs * 8 * 256);
-  const uint32_t a_soff0 = (uint32_t)((mb0 >> 3) * ksteps * 8 * 1024);
-  const uint32_t i_soff0 = (uint32_t)((mb0 >> 3) * kpairs * 8 * 256);
-  const uint32_t a_voff = 16 * lane, i_voff = 4 * lane;
-  u32x4 a_buf[2][kRB];
-  uint32_t i_buf[2][kRB];
-
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(xv, mgroups * ksteps * 8192);
+  const __amdgpu_buffer_rsrc_t ir = make_rsrc(xi, mgroups * ksteps * 1024);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, N * K * 2);
+  const uint32_t a_group0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 8192));
+  const uint32_t i_group0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 1024));
+  const uint32_t a_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 8192));
+  const uint32_t i_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 1024));
   const WTileOffsets wo = w_tile_offsets(K, n0);
-  const char* stage_base = &lds[0][0] + 16 * lane + wn * kCB * 2048;
-
-  // Vector-memory operations per thread in one W copy.
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(&lds[0]);
   constexpr int kWOps = KM == kAligned8 ? 4 * kWChunksPerThread : kWChunksPerThread;
+  constexpr int kStepOps = kWOps + 6;
 
-  auto prefetch_w = [&](int64_t ks, auto stage_c) {
+  auto prefetch = [&](int64_t ks, auto stage_c) {
     constexpr int b = decltype(stage_c)::value;
-    if constexpr (KM == kAligned8) dma_w_tile_dword(wr, N, K, n0, ks * kTileK, lds[b]);
-    else dma_w_tile<KM == kAligned16>(wr, wo, K, ks * kTileK, lds[b]);
+    const uint32_t st = lds_base + b * kStageBytes;
+    dma_a_tile_asm(ar, ir, a_group0, i_group0, a_gstride, i_gstride, ks, st);
+    if constexpr (KM == kAligned8) dma_w_tile_dword(wr, N, K, n0, ks * kTileK, &lds[b * kStageBytes]);
+    else dma_w_tile_asm(wr, wo, K, ks * kTileK, st, KM == kAligned16);
   };
-  auto prefetch_a = [&](int64_t ks, auto buf_c) {
-    constexpr int b = decltype(buf_c)::value;
-    const uint32_t so = a_soff0 + (uint32_t)(ks * 8 * 1024);
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) a_buf[b][rb] = buf_load16(ar, a_voff, so + rb * 1024);
-    const uint32_t si = i_soff0 + (uint32_t)((ks >> 1) * 8 * 256);
+
+  const char* b_base = &lds[0] + 16 * lane + wn * kCB * 2048;
+  const char* a_base = &lds[0] + kAStageOff + 16 * lane + wm * 8192;
+  const char* i_base = &lds[0] + kIStageOff + 16 * lane + wm * 1024;
+
+  // One k-step ks in stage b = ks % 3: wait until only step ks + 1's copies
+  // are in flight, barrier (stage b complete for every wave; every wave done
+  // with stage (b + 2) % 3), start the copies of step ks + 2, then the
+  // matrix work: 8 A fragments and their position fields from LDS, the W
+  // fragments one column block ahead, 64 structured-sparse MFMAs.  The
+  // position fields of row blocks 2j and 2j+1 share a 32-bit word (abid).
+  auto step = [&](int64_t ks, auto b_c) {
+    constexpr int b = decltype(b_c)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<kStepOps>();
+    barrier_no_fence();
+    const int64_t kn = ks + 2 < ksteps ? ks + 2 : ksteps - 1;
+    prefetch(kn, std::integral_constant<int, (b + 2) % kStages>{});
+    __builtin_amdgcn_sched_barrier(0);
+    const u32x4 iw = *reinterpret_cast<const u32x4*>(i_base + b * kStageBytes);
+    bf16x8 af[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
-      i_buf[b][rb] = __builtin_amdgcn_raw_buffer_load_b32(ir, i_voff + rb * 256, si, 0);
-  };
-
-  // One k-step ks (W stage ks % 3, A buffer and index half ks % 2).  Each
-  // step issues, in this order, the A loads of step ks + 1 and the W copy of
-  // step ks + 2; so at the top of step ks the only operations allowed to be
-  // in flight are the W copy of step ks + 1 (kWOps).  The barrier then
-  // publishes stage ks % 3 and guarantees that every wave is done with
-  // stage (ks + 2) % 3.  The W fragments are read from LDS one column block
-  // ahead of the MFMAs.  With the stage a compile-time constant the
-  // compiler sees that the copy into stage (ks + 2) % 3 does not alias the
-  // reads of stage ks % 3, and does not wait for it.
-  auto step = [&](int64_t ks, auto b_c, auto h_c) {
-    constexpr int b = decltype(b_c)::value;
-    constexpr int h = decltype(h_c)::value;
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm<kWOps>();
-    barrier_no_fence();
-    const int64_t ka = ks + 1 < ksteps ? ks + 1 : ksteps - 1;
-    const int64_t kw = ks + 2 < ksteps ? ks + 2 : ksteps - 1;
-    prefetch_a(ka, std::integral_constant<int, 1 - h>{});
-    prefetch_w(kw, std::integral_constant<int, (b + 2) % kStages>{});
-    __builtin_amdgcn_sched_barrier(0);
-    const char* stage = stage_base + b * kWTileBytes;
+      af[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_base + b * kStageBytes + rb * 1024));
+    const char* stage = b_base + b * kStageBytes;
     u32x4 b0 = *reinterpret_cast<const u32x4*>(stage);
     u32x4 b1 = *reinterpret_cast<const u32x4*>(stage + 1024);
 #pragma unroll
@@ -114,38 +160,26 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint32_t* __restrict__ xi
         b1 = *reinterpret_cast<const u32x4*>(stage + (cb + 1) * 2048 + 1024);
       }
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb)
-        acc[rb][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a_buf[h][rb]), bf,
-                                                                acc[rb][cb], (int)i_buf[h][rb], 0, h);
+      for (int rb = 0; rb < kRB; rb += 2) {
+        acc[rb][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb], bf, acc[rb][cb], (int)iw[rb / 2], 0, 0);
+        acc[rb + 1][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb + 1], bf, acc[rb + 1][cb], (int)iw[rb / 2], 0, 1);
+      }
     }
   };
 
-  // Prologue: W of steps 0 and 1, A of step 0, in the order the steps assume.
-  prefetch_w(0, std::integral_constant<int, 0>{});
-  prefetch_a(0, std::integral_constant<int, 0>{});
-  prefetch_w(ksteps > 1 ? 1 : 0, std::integral_constant<int, 1>{});
+  prefetch(0, std::integral_constant<int, 0>{});
+  prefetch(ksteps > 1 ? 1 : 0, std::integral_constant<int, 1>{});
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  // ksteps is even; steps run in groups of six so that the stage (ks % 3)
-  // and the A buffer / index half (ks % 2) are compile-time constants.
   int64_t ks = 0;
-  for (; ks + 6 <= ksteps; ks += 6) {
-    step(ks + 0, I0{}, I0{});
-    step(ks + 1, I1{}, I1{});
-    step(ks + 2, I2{}, I0{});
-    step(ks + 3, I0{}, I1{});
-    step(ks + 4, I1{}, I0{});
-    step(ks + 5, I2{}, I1{});
+  for (; ks + 3 <= ksteps; ks += 3) {
+    step(ks + 0, I0{});
+    step(ks + 1, I1{});
+    step(ks + 2, I2{});
   }
-  if (ks < ksteps) {            // 2 or 4 steps left
-    step(ks + 0, I0{}, I0{});
-    step(ks + 1, I1{}, I1{});
-    if (ks + 2 < ksteps) {
-      step(ks + 2, I2{}, I0{});
-      step(ks + 3, I0{}, I1{});
-    }
-  }
+  if (ks < ksteps) step(ks, I0{});
+  if (ks + 1 < ksteps) step(ks + 1, I1{});
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
 
@@ -208,7 +242,7 @@ hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const ui
   const WsLayout L = ws_layout(M, K, r);
   const char* ws = static_cast<const char*>(workspace);
   const u32x4* xv = reinterpret_cast<const u32x4*>(ws + L.off_xv);
-  const uint32_t* xi = reinterpret_cast<const uint32_t*>(ws + L.off_xi);
+  const uint16_t* xi = reinterpret_cast<const uint16_t*>(ws + L.off_xi);
   const float* s = reinterpret_cast<const float*>(ws + L.off_s);
   const u32x4* t = reinterpret_cast<const u32x4*>(ws + L.off_t);
   const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
