@@ -7,10 +7,8 @@
 // matrix instruction.
 //
 // The A tile (256 tokens x 64 channels of X per step) goes through LDS in
-// the same operand order as W -- for each 16-token block and 32-channel
-// half, 64 lanes x 16 bytes, lane l holding token l % 16, channels
-// 8 (l / 16) + [0, 8) -- copied by the same DMA routine, in a 2-stage ring
-// next to the 3-stage W ring (96 + 64 KiB of LDS).
+// the same swizzled row-major layout as W, copied by the same DMA routine,
+// in a 2-stage ring next to the 3-stage W ring (96 + 64 KiB of LDS).
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -25,8 +23,12 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
 dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                   int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y) {
   constexpr int kWStages = 3, kAStages = 2;
-  __shared__ __attribute__((aligned(16))) char lds_w[kWStages][kWTileBytes];
-  __shared__ __attribute__((aligned(16))) char lds_a[kAStages][kWTileBytes];
+  // One LDS block: the W ring, then the A ring; the epilogue reuses all of it.
+  constexpr int kLdsBytes = (kWStages + kAStages) * kWTileBytes;
+  static_assert(kStoreLdsBytes <= kLdsBytes, "store staging must fit in the rings");
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  char* const lds_w = lds;
+  char* const lds_a = lds + kWStages * kWTileBytes;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
   const int wm = wave >> 1, wn = wave & 1;
@@ -49,8 +51,11 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, N * K * 2);
   const WTileOffsets xo = w_tile_offsets(K, m0);
   const WTileOffsets wo = w_tile_offsets(K, n0);
-  const char* b_base = &lds_w[0][0] + 16 * lane + wn * kCB * 2048;
-  const char* a_base = &lds_a[0][0] + 16 * lane + wm * kRB * 2048;
+  const uint32_t f0 = frag_lane_offset(0), f1 = frag_lane_offset(1);
+  const char* b_base0 = lds_w + wn * kCB * 2048 + f0;
+  const char* b_base1 = lds_w + wn * kCB * 2048 + f1;
+  const char* a_base0 = lds_a + wm * kRB * 2048 + f0;
+  const char* a_base1 = lds_a + wm * kRB * 2048 + f1;
   constexpr int kTileOps = KM == kAligned8 ? 4 * kWChunksPerThread : kWChunksPerThread;
 
   // Both tile copies are issued as inline-asm DMA blocks: no vector-memory
@@ -79,25 +84,27 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
     barrier_no_fence();
     const int64_t ka = ks + 1 < ksteps ? ks + 1 : ksteps - 1;
     const int64_t kw = ks + 2 < ksteps ? ks + 2 : ksteps - 1;
-    copy_tile(xr, xo, m0, M, ka, lds_a[1 - ba]);
-    copy_tile(wr, wo, n0, N, kw, lds_w[(bw + 2) % kWStages]);
+    copy_tile(xr, xo, m0, M, ka, lds_a + (1 - ba) * kWTileBytes);
+    copy_tile(wr, wo, n0, N, kw, lds_w + (bw + 2) % kWStages * kWTileBytes);
     __builtin_amdgcn_sched_barrier(0);
-    const char* bs = b_base + bw * kWTileBytes;
-    const char* as = a_base + ba * kWTileBytes;
+    const char* bs0 = b_base0 + bw * kWTileBytes;
+    const char* bs1 = b_base1 + bw * kWTileBytes;
+    const char* as0 = a_base0 + ba * kWTileBytes;
+    const char* as1 = a_base1 + ba * kWTileBytes;
     bf16x8 af[2][kRB];
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        af[h][rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + rb * 2048 + h * 1024));
-    u32x4 q0 = *reinterpret_cast<const u32x4*>(bs);
-    u32x4 q1 = *reinterpret_cast<const u32x4*>(bs + 1024);
+    for (int rb = 0; rb < kRB; ++rb) {
+      af[0][rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as0 + rb * 2048));
+      af[1][rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as1 + rb * 2048));
+    }
+    u32x4 q0 = *reinterpret_cast<const u32x4*>(bs0);
+    u32x4 q1 = *reinterpret_cast<const u32x4*>(bs1);
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
       const bf16x8 b0 = __builtin_bit_cast(bf16x8, q0), b1 = __builtin_bit_cast(bf16x8, q1);
       if (cb + 1 < kCB) {
-        q0 = *reinterpret_cast<const u32x4*>(bs + (cb + 1) * 2048);
-        q1 = *reinterpret_cast<const u32x4*>(bs + (cb + 1) * 2048 + 1024);
+        q0 = *reinterpret_cast<const u32x4*>(bs0 + (cb + 1) * 2048);
+        q1 = *reinterpret_cast<const u32x4*>(bs1 + (cb + 1) * 2048);
       }
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
@@ -108,9 +115,9 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
     }
   };
 
-  copy_tile(wr, wo, n0, N, 0, lds_w[0]);
-  copy_tile(xr, xo, m0, M, 0, lds_a[0]);
-  copy_tile(wr, wo, n0, N, ksteps > 1 ? 1 : 0, lds_w[1]);
+  copy_tile(wr, wo, n0, N, 0, lds_w);
+  copy_tile(xr, xo, m0, M, 0, lds_a);
+  copy_tile(wr, wo, n0, N, ksteps > 1 ? 1 : 0, lds_w + kWTileBytes);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -131,8 +138,10 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
   if (ks + 4 < ksteps) step(ks + 4, I1{}, I0{});
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
+  barrier_no_fence();                     // every wave is done with the rings
 
-  store_acc_bf16(acc, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
+  if (N % 8 == 0) store_tile_via_lds(acc, lds, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
+  else store_acc_bf16(acc, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
 }
 
 }  // namespace

@@ -54,77 +54,68 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 // rows are only 8-byte aligned (8-byte loads, guarded per group).
 enum KMode { kFullK = 0, kAligned16 = 1, kAligned8 = 2 };
 
-// Byte offsets (at channel 0) of the thread's 8 chunks of a W tile: one
-// per-lane base (row n0 + 64 wave + l % 16, channel 8 (l / 16)) plus a
-// uniform per-chunk step (16 (i / 2) rows, 32 (i % 2) channels), so only one
-// VGPR stays live.  Rows past N lie past the end of W and read as zeros
+// A 256-row x 64-channel bf16 tile in LDS (the W tile, and the X tile of
+// the dense kernel): row-major, 128 bytes per row, with the 16-byte chunk c
+// (channels 8c .. 8c + 7) of row n stored in slot c ^ (n & 7) of the row.
+// The copy then reads whole 128-byte lines of the row-major source (8 lanes
+// per row), and a fragment read -- 16 rows at one chunk index -- spreads over
+// all LDS banks.
+//
+// Copy: instruction i of wavefront v moves rows 64 v + 8 i + [0, 8); lane l
+// fills LDS slot l % 8 of row l / 8 (the DMA writes lane l's 16 bytes to
+// M0 + 16 l) with source chunk (l % 8) ^ (l / 8).  Byte offsets (at channel
+// 0) are one per-lane base plus a uniform 8-row step, so one VGPR stays
+// live; rows past the end of the tensor lie past its end and read as zeros
 // (the row is in the VGPR offset, which the buffer range check covers).
 struct WTileOffsets {
   uint32_t base;                  // VGPR
-  uint32_t row16;                 // uniform: bytes of 16 rows
-  int32_t k_lane;                 // 8 (l / 16)
-  __device__ __forceinline__ uint32_t off(int i) const {
-    return base + (uint32_t)(i / 2) * row16 + (uint32_t)(i % 2) * 64u;
-  }
+  uint32_t row8;                  // uniform: bytes of 8 rows
+  int32_t k_lane;                 // 8 ((l % 8) ^ (l / 8))
+  __device__ __forceinline__ uint32_t off(int i) const { return base + (uint32_t)i * row8; }
 };
 
 __device__ __forceinline__ WTileOffsets w_tile_offsets(int64_t K, int64_t n0) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   WTileOffsets o;
-  o.k_lane = 8 * (lane >> 4);
-  o.base = (uint32_t)(((n0 + 64 * wave + (lane & 15)) * K + o.k_lane) * 2);
-  o.row16 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * K * 2));
+  o.k_lane = 8 * ((lane & 7) ^ (lane >> 3));
+  o.base = (uint32_t)(((n0 + 64 * wave + (lane >> 3)) * K + o.k_lane) * 2);
+  o.row8 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * K * 2));
   return o;
+}
+
+// Per-lane byte offset, inside a 16-row block of such a tile, of the lane's
+// fragment for k-half h (channels 32 h + 8 (l / 16) + [0, 8) of row l % 16):
+// the operand order of v_mfma_f32_16x16x32_bf16 (both operands) and the
+// two halves of v_smfmac_f32_16x16x64_bf16's B operand.  Row block b adds
+// 2048 b.
+__device__ __forceinline__ uint32_t frag_lane_offset(int h) {
+  const int lane = threadIdx.x & 63;
+  return (uint32_t)((lane & 15) * 128 + (((4 * h + (lane >> 4)) ^ (lane & 7)) << 4));
 }
 
 // Byte offset that lies past every tensor: a buffer load there returns zeros.
 constexpr uint32_t kOobOffset = 0xfffffff0u;
 
-// Direct global -> LDS copy of the W tile at channel k0 (K % 8 == 0): each
-// buffer_load_dwordx4 ... lds writes lane l's 16 bytes to base + 16 l, so
-// chunk i of every lane lands at (2 cb + h) * 1024 + 16 l without touching
-// registers.  Chunks past K are pointed out of the buffer and arrive as
-// zeros.  The caller waits on vmcnt before the barrier that publishes them.
-template <bool GUARD_K>
-__device__ __forceinline__ void dma_w_tile(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
-                                           int64_t k0, char* lds_stage) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t soff = (uint32_t)(k0 * 2);
-#pragma unroll
-  for (int i = 0; i < kWChunksPerThread; ++i) {
-    uint32_t voff = o.off(i);
-    if constexpr (GUARD_K) {
-      const int64_t k = k0 + 32 * (i % 2) + o.k_lane;
-      voff = (k + 8 <= K) ? voff : kOobOffset - soff;
-    }
-    char* dst = lds_stage + (2 * (4 * wave + i / 2) + i % 2) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(dst), 16, voff, soff, 0, 0);
-  }
-}
-
-// The same copy issued as one inline-asm block of 8 buffer_load_dwordx4 ...
-// lds instructions.  The compiler does not see these loads, so it never
-// inserts vmcnt waits for them (with the builtin it sometimes cannot prove
-// that a copy into one stage does not alias reads of another, and drains
-// all loads); the caller accounts for them with explicit vmcnt waits.  The
-// block has no output registers -- the data goes to LDS -- and writes only
-// M0, which it saves and restores; it uses no instruction that sets SCC.
-// s_nop 4 covers a VALU write of an SGPR operand right before the block.
+// The tile copy at channel k0 (K % 8 == 0) as one inline-asm block of 8
+// buffer_load_dwordx4 ... lds instructions.  The compiler does not see these
+// loads, so it never inserts vmcnt waits for them (with the builtin it
+// sometimes cannot prove that a copy into one stage does not alias reads of
+// another, and drains all loads); the caller accounts for them with
+// explicit vmcnt waits.  The block has no output registers -- the data goes
+// to LDS -- and writes only M0, which it saves and restores; it uses no
+// instruction that sets SCC.  s_nop 4 covers a VALU write of an SGPR operand
+// right before the block.  With guard_k, chunks past K are pointed out of
+// the buffer and arrive as zeros.
 __device__ __forceinline__ void dma_w_tile_asm(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
                                                int64_t k0, uint32_t lds_stage_addr, bool guard_k) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(k0 * 2));
+  const bool chunk_ok = !guard_k || k0 + o.k_lane + 8 <= K;
   uint32_t v[kWChunksPerThread];
 #pragma unroll
-  for (int i = 0; i < kWChunksPerThread; ++i) {
-    v[i] = o.off(i);
-    if (guard_k) {
-      const int64_t k = k0 + 32 * (i % 2) + o.k_lane;
-      v[i] = (k + 8 <= K) ? v[i] : kOobOffset - soff;
-    }
-  }
-  // LDS byte address of chunk i: stage + (2 (4 wave + i / 2) + i % 2) * 1024
-  // = stage + 8192 wave + 1024 i.  All eight are computed outside the block,
+  for (int i = 0; i < kWChunksPerThread; ++i) v[i] = chunk_ok ? o.off(i) : kOobOffset - soff;
+  // LDS byte address of instruction i: stage + 128 (64 wave + 8 i) =
+  // stage + 8192 wave + 1024 i.  All eight are computed outside the block,
   // which then only moves them into M0 (s_mov does not touch SCC).
   const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_stage_addr + 8192u * (uint32_t)wave);
   uint32_t saved;
@@ -157,25 +148,24 @@ __device__ __forceinline__ void dma_w_tile_asm(__amdgpu_buffer_rsrc_t wr, const 
   (void)saved;
 }
 
-// W-tile copy for K % 8 == 4 (rows only 8-byte aligned): 32 dword DMAs per
+// Tile copy for K % 8 == 4 (rows only 8-byte aligned): 32 dword DMAs per
 // thread through the builtin, which the compiler tracks (and drains before
 // later LDS reads -- slow, but this mode only serves odd channel counts).
-// DMA lane j of instruction (b, q) carries dword j % 4 of the chunk of lane
-// 16 q + j / 4 in chunk block b, so the LDS layout matches the 16-byte copy.
+// Instruction b of wavefront v fills rows 64 v + 2 b + [0, 2); DMA lane j
+// writes dword j % 4 of slot (j % 32) / 4 of row j / 32, so the LDS layout
+// matches the 16-byte copy.
 __device__ __forceinline__ void dma_w_tile_dword(__amdgpu_buffer_rsrc_t wr, int64_t N, int64_t K, int64_t n0,
                                                  int64_t k0, char* lds_stage) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int b = 0; b < kWChunksPerThread; ++b) {
-    const int cb = 4 * wave + b / 2, h = b % 2;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t n = n0 + 16 * cb + (lane >> 2);
-      const int64_t k = k0 + 32 * h + 8 * q + 2 * (lane & 3);
-      const uint32_t voff = (k + 2 <= K && n < N) ? (uint32_t)((n * K + k) * 2) : kOobOffset;
-      char* dst = lds_stage + (2 * cb + h) * 1024 + 256 * q;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(dst), 4, voff, 0, 0, 0);
-    }
+  for (int b = 0; b < 32; ++b) {
+    const int row = 64 * wave + 2 * b + (lane >> 5);
+    const int chunk = ((lane & 31) >> 2) ^ (row & 7);
+    const int64_t n = n0 + row;
+    const int64_t k = k0 + 8 * chunk + 2 * (lane & 3);
+    const uint32_t voff = (k + 2 <= K && n < N) ? (uint32_t)((n * K + k) * 2) : kOobOffset;
+    char* dst = lds_stage + (64 * wave + 2 * b) * 128;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(dst), 4, voff, 0, 0, 0);
   }
 }
 
@@ -191,46 +181,6 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-
-// Register copy of the W tile for K % 8 == 4 (rows only 8-byte aligned).
-__device__ __forceinline__ void load_w_tile_8(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
-                                              int64_t k0, u32x4 (&st)[kWChunksPerThread]) {
-  const uint32_t soff = (uint32_t)(k0 * 2);
-#pragma unroll
-  for (int i = 0; i < kWChunksPerThread; ++i) {
-    const int64_t k = k0 + 32 * (i % 2) + o.k_lane;
-    u32x4 v = (u32x4){0, 0, 0, 0};
-    if (k + 4 <= K) { const u32x2 a = buf_load8(wr, o.off(i), soff); v[0] = a[0]; v[1] = a[1]; }
-    if (k + 8 <= K) { const u32x2 b = buf_load8(wr, o.off(i) + 8, soff); v[2] = b[0]; v[3] = b[1]; }
-    st[i] = v;
-  }
-}
-
-__device__ __forceinline__ void store_w_tile(char* lds_stage, const u32x4 (&st)[kWChunksPerThread]) {
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int i = 0; i < kWChunksPerThread; ++i) {
-    const int cb = 4 * wave + i / 2, h = i % 2;
-    *reinterpret_cast<u32x4*>(lds_stage + (2 * cb + h) * 1024 + 16 * lane) = st[i];
-  }
-}
-
-// Starts the copy of the W tile of channel k0 into an LDS stage.  DMA modes
-// finish on their own (vmcnt); the register mode holds the data in `st`
-// until commit_w_tile writes it.
-template <int KM, int NS>
-__device__ __forceinline__ void issue_w_tile(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
-                                             int64_t k0, char* lds_stage, u32x4 (&st)[NS]) {
-  if constexpr (KM == kAligned8) load_w_tile_8(wr, o, K, k0, st);
-  else dma_w_tile<KM == kAligned16>(wr, o, K, k0, lds_stage);
-}
-
-template <int KM, int NS>
-__device__ __forceinline__ void commit_w_tile(char* lds_stage, const u32x4 (&st)[NS]) {
-  if constexpr (KM == kAligned8) store_w_tile(lds_stage, st);
-}
-
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs
 // (workgroup id i runs on XCD i % 8), and each XCD has its own L2.  The id
@@ -275,17 +225,17 @@ __device__ __forceinline__ void store_acc_bf16(const f32x4 (&acc)[kRB][kCB], uin
 }
 
 // Epilogue store through LDS.  Each wavefront writes its 128 x 128 tile
-// as bf16 into its own LDS region (row pitch 288 bytes: the 32-byte row
-// segments of the 4 row groups of one write land on distinct banks), then
-// reads it back 16 bytes per lane along rows and issues 32 coalesced 16-byte
-// buffer stores (4 rows of 256 bytes each) instead of 256 scattered 2-byte
-// stores.  The caller must have drained every DMA and passed a barrier, so
-// that the LDS ring is free (needs 4 x 36 KiB).  Rows past M lie past the
-// end of Y and are dropped by the buffer range check; column chunks past N
-// are pointed out of range (N % 8 == 0 is required: a chunk is all in or
-// all out).
-constexpr int kStorePitch = 288;
-constexpr int kStoreRegion = kWaveM * kStorePitch;      // 36 KiB per wavefront
+// as bf16 into its own LDS region (row pitch 272 bytes: 16-byte aligned
+// rows, and the four row groups of one write are 16 banks apart), then reads it back 16 bytes
+// per lane along rows and issues 32 coalesced 16-byte buffer stores (4 rows
+// x 256 bytes each) instead of 256 scattered 2-byte stores.  The caller
+// must have drained every DMA and passed a barrier, so that the LDS ring is
+// free (4 x 34 KiB).  Requires N % 8 == 0 (a chunk of 8 columns is all
+// inside or all outside Y); chunks past M or N are pointed out of range,
+// and the whole offset is in the VGPR operand.
+constexpr int kStorePitch = 272;
+constexpr int kStoreRegion = kWaveM * kStorePitch;      // 34 KiB per wavefront
+constexpr int kStoreLdsBytes = 4 * kStoreRegion;
 
 __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[kRB][kCB], char* lds_base,
                                                    uint16_t* __restrict__ y, int64_t M, int64_t N,
@@ -309,14 +259,14 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[kRB][kCB],
   const int64_t col = n0 + 8 * chunk;
   const bool col_ok = col + 8 <= N;
   const uint32_t lane_off = (uint32_t)(((m0 + sub_row) * N + col) * 2);
-  const uint32_t row4 = __builtin_amdgcn_readfirstlane((uint32_t)(4 * N * 2));
+  const uint32_t row4 = (uint32_t)(4 * N * 2);
 #pragma unroll
   for (int it = 0; it < kWaveM / 4; ++it) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(region + (4 * it + sub_row) * kStorePitch + 16 * chunk);
-    const uint32_t soff = (uint32_t)it * row4;
-    const uint32_t voff = col_ok ? lane_off : kOobOffset - soff;
+    const bool ok = col_ok && m0 + 4 * it + sub_row < M;
+    const uint32_t voff = ok ? lane_off + (uint32_t)it * row4 : kOobOffset;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), yr,
-                                           voff, soff, 0);
+                                           voff, 0, 0);
   }
 }
 

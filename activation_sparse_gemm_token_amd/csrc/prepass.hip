@@ -13,8 +13,11 @@
 //
 // Both terms are 2:4-sparse products of exact input words, so they run on the
 // structured-sparse matrix cores with the kept and the pruned halves of each
-// group, and no cancellation happens in fp32.  alpha*T is stored as a bf16
-// hi/lo pair in the dense 16x16x32 A-operand order for the GEMM epilogue.
+// group, and no cancellation happens in fp32.  alpha*T/s is stored as a
+// bf16 hi/lo pair in the dense 16x16x32 A-operand order: divided by the
+// token's scale (s >= 1), so that the GEMM can accumulate the LoRA-up
+// product into the same fp32 accumulators as the sparse product and apply
+// s once at the end, Y = s (S(X) W^T + (alpha T / s) B^T).
 //
 // Selection happens here, once per element, and not in the GEMM prologue:
 // there it would be repeated for every N tile, and its VALU cost (about 30
@@ -214,7 +217,7 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
           float a = 0.f;
 #pragma unroll
           for (int w = 0; w < kWaves; ++w) a += red_t[w][rr][col];
-          v[e] = alpha * a;
+          v[e] = alpha * a / s_sh[rr];
         }
         const uint32_t h = pack_bf16x2(v[0], v[1]);
         hi[j / 2] = h;

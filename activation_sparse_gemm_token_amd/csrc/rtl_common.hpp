@@ -27,7 +27,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 //       groups), [mb / 8][k-step][lane][mb % 8] x 2 bytes, so one 16-byte
 //       read gives a lane the fields of all 8 row blocks;
 //   s:  per-token scale, fp32 [mp];
-//   t:  alpha * T as bf16 hi and lo, [mb][r-step][hi, lo][lane] x 16 bytes.
+//   t:  alpha * T / s as bf16 hi and lo, [mb][r-step][hi, lo][lane] x 16 bytes.
 // ---------------------------------------------------------------------------
 struct WsLayout {
   int64_t mp, kp, rp;

@@ -30,6 +30,27 @@ bool dims_ok(int64_t M, int64_t K) {
   return M >= 0 && K >= 4 && K % 4 == 0 && M < kMaxDim && K < kMaxDim;
 }
 
+// The GEMM kernels address each tensor through a buffer resource with a
+// 32-bit size and 32-bit offsets.
+constexpr int64_t kMaxBytes = (int64_t)1 << 31;
+
+bool bytes_ok(int64_t rows, int64_t cols, int64_t elem) {
+  return rows == 0 || cols == 0 || (cols <= kMaxBytes / elem && rows < kMaxBytes / (cols * elem));
+}
+
+// Every tensor and workspace region of a linear-layer call below 2 GiB,
+// counting the up to 255 rows past the end that the last 256-row tile of
+// X, W and Y addresses (they read as zeros / are not written).
+bool layer_sizes_ok(int64_t M, int64_t N, int64_t K, int64_t r) {
+  const int64_t pad = 256;
+  if (!bytes_ok(M + pad, K, 2) || !bytes_ok(N + pad, K, 2) || !bytes_ok(M + pad, N, 2) ||
+      !bytes_ok(r, K, 2) || !bytes_ok(N + pad, r, 2))
+    return false;
+  if (M == 0) return true;
+  const rtl::WsLayout L = rtl::ws_layout(M, K, r);
+  return bytes_ok(L.mp, L.kp, 1) && bytes_ok(L.mp, L.rp, 4);
+}
+
 rtl_status check_device() {
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
@@ -74,7 +95,7 @@ RTL_API rtl_status rtl_sparsify_2of4(const uint16_t* x, int64_t M, int64_t K, ui
 }
 
 RTL_API size_t rtl_sparse_linear_workspace_bytes(int64_t M, int64_t K, int64_t r) {
-  if (!dims_ok(M, K) || r < 0 || r > RTL_MAX_LORA_RANK) return 0;
+  if (!dims_ok(M, K) || r < 0 || r > RTL_MAX_LORA_RANK || !layer_sizes_ok(M, 0, K, r)) return 0;
   if (M == 0) return 0;
   return rtl::ws_layout(M, K, r).total;
 }
@@ -83,6 +104,7 @@ RTL_API rtl_status rtl_sparse_linear_prepare(const uint16_t* x, const uint16_t* 
                                              int64_t K, int64_t r, float lora_scale, void* workspace,
                                              size_t workspace_bytes, void* hip_stream) {
   if (!dims_ok(M, K) || r < 0 || r > RTL_MAX_LORA_RANK) return RTL_ERR_BAD_SHAPE;
+  if (!layer_sizes_ok(M, 0, K, r)) return RTL_ERR_BAD_SHAPE;
   if (M == 0) return RTL_OK;
   if (x == nullptr) return RTL_ERR_NULL_POINTER;
   if (r > 0 && lora_a == nullptr) return RTL_ERR_NULL_POINTER;
@@ -100,6 +122,7 @@ RTL_API rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspa
                                            int64_t N, int64_t K, int64_t r, uint16_t* y,
                                            void* hip_stream) {
   if (!dims_ok(M, K) || N < 0 || N >= kMaxDim || r < 0 || r > RTL_MAX_LORA_RANK) return RTL_ERR_BAD_SHAPE;
+  if (!layer_sizes_ok(M, N, K, r)) return RTL_ERR_BAD_SHAPE;
   if (M == 0 || N == 0) return RTL_OK;
   if (w == nullptr || y == nullptr) return RTL_ERR_NULL_POINTER;
   if (r > 0 && lora_b == nullptr) return RTL_ERR_NULL_POINTER;
@@ -117,6 +140,7 @@ RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const
                                      int64_t r, float lora_scale, uint16_t* y, void* workspace,
                                      size_t workspace_bytes, void* hip_stream) {
   if (!dims_ok(M, K) || N < 0 || N >= kMaxDim || r < 0 || r > RTL_MAX_LORA_RANK) return RTL_ERR_BAD_SHAPE;
+  if (!layer_sizes_ok(M, N, K, r)) return RTL_ERR_BAD_SHAPE;
   if (M == 0 || N == 0) return RTL_OK;
   if (x == nullptr || w == nullptr || y == nullptr) return RTL_ERR_NULL_POINTER;
   if (r > 0 && (lora_a == nullptr || lora_b == nullptr)) return RTL_ERR_NULL_POINTER;
@@ -135,6 +159,7 @@ RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const
 RTL_API rtl_status rtl_dense_linear(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                                     int64_t K, uint16_t* y, void* hip_stream) {
   if (!dims_ok(M, K) || N < 0 || N >= kMaxDim) return RTL_ERR_BAD_SHAPE;
+  if (!layer_sizes_ok(M, N, K, 0)) return RTL_ERR_BAD_SHAPE;
   if (M == 0 || N == 0) return RTL_OK;
   if (x == nullptr || w == nullptr || y == nullptr) return RTL_ERR_NULL_POINTER;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return RTL_ERR_MISALIGNED;
@@ -147,7 +172,7 @@ RTL_API const char* rtl_status_string(rtl_status s) {
   switch (s) {
     case RTL_OK: return "ok";
     case RTL_ERR_NULL_POINTER: return "a required pointer is NULL";
-    case RTL_ERR_BAD_SHAPE: return "invalid shape (sizes must be >= 0, K >= 4 and K % 4 == 0, r <= RTL_MAX_LORA_RANK)";
+    case RTL_ERR_BAD_SHAPE: return "invalid shape (sizes must be >= 0, K >= 4 and K % 4 == 0, r <= RTL_MAX_LORA_RANK, every tensor below 2 GiB)";
     case RTL_ERR_MISALIGNED: return "a base pointer is not 16-byte aligned";
     case RTL_ERR_WORKSPACE: return "workspace missing or smaller than rtl_sparse_linear_workspace_bytes()";
     case RTL_ERR_NO_DEVICE: return "no HIP device is visible";

@@ -3,15 +3,18 @@
 //
 //   Y[m, n] = bf16( s[m] * sum_k (M*X)[m, k] W[n, k]  +  sum_j (alpha T)[m, j] B[n, j] )
 //
+// computed as Y = bf16( s * ( S(X) W^T + (alpha T / s) B^T ) ).
+//
 // The compressed activation comes from the pre-pass already in the register
 // order of v_smfmac_f32_16x16x64_bf16's A operand (lane l: token l % 16, kept
 // values of channels 16 (l / 16) + [0, 16), 2-bit positions in a 16-bit
-// field; two k-steps share one 32-bit index word, picked with the abid
-// operand).  Each wavefront loads its A fragments straight from global
-// memory (1 KiB contiguous per fragment) and its W fragments from LDS.  The
-// scale is applied to the fp32 accumulators, never folded into a bf16
-// operand, and the LoRA-up runs as dense 16x16x32 MFMAs on the hi and lo
-// halves of alpha*T.
+// field; the fields of two 16-token blocks share one 32-bit word, picked
+// with the abid operand).  Every operand reaches LDS by DMA through one
+// 3-stage ring: first the K/64 structured-sparse k-steps, then r/32 LoRA
+// steps that run dense 16x16x32 MFMAs on the hi and lo halves of
+// alpha T / s (pre-pass) against B, into the same accumulators.  The scale
+// is applied once to the fp32 accumulators, never folded into a bf16
+// operand, and the tile leaves through LDS as coalesced 16-byte stores.
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -23,9 +26,15 @@ namespace {
 
 // Per k-step LDS stage: the W tile (32 KiB), the workgroup's 256 rows of
 // compressed A (16 x 1 KiB fragments) and their position fields (2 x 1 KiB).
+// A LoRA step puts the 256 rows of alpha T / s (16 blocks x hi, lo x 1 KiB)
+// where W goes and the 256 columns of B (16 x 1 KiB) where A goes.
 constexpr int kAStageOff = kWTileBytes;
 constexpr int kIStageOff = kWTileBytes + 16 * 1024;
 constexpr int kStageBytes = kWTileBytes + 18 * 1024;
+constexpr int kStages = 3;                                   // prefetch distance 2
+constexpr int kScaleOff = kStages * kStageBytes;             // 256 per-token scales
+constexpr int kLdsBytes = kScaleOff + 1024;
+static_assert(kStoreLdsBytes <= kScaleOff, "store staging must not reach the scales");
 
 // Copies the compressed A operand of one k-step into an LDS stage: thread
 // (wave v, i) moves fragment c = 4 v + i (16-token block c % 8 of group
@@ -77,15 +86,110 @@ __device__ __forceinline__ void dma_a_tile_asm(__amdgpu_buffer_rsrc_t ar, __amdg
   (void)saved;
 }
 
-template <int KM>
+// Copies the operands of LoRA step rs into an LDS stage: thread (wave v,
+// i < 8) moves 1 KiB of alpha T / s (16-token block 4 v + i / 2, half i % 2)
+// and thread (v, i < 4) 1 KiB of B (columns n0 + 16 (4 v + i) + [0, 16),
+// ranks 32 rs + 8 (l / 16) + [0, 8)).  B rows past N and rank chunks past r
+// carry their whole offset in the VGPR operand and read as zeros.  The last
+// two B copies are issued twice, so that a LoRA step issues as many
+// vector-memory operations (14) as a k-step and the waits stay uniform.
+__device__ __forceinline__ void dma_lora_tile_asm(__amdgpu_buffer_rsrc_t tr, __amdgpu_buffer_rsrc_t br,
+                                                  uint32_t t_block0, int64_t rsteps, int64_t rs,
+                                                  int64_t N, int64_t r, int64_t n0, uint32_t lds_stage_addr) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t blk = __builtin_amdgcn_readfirstlane((uint32_t)(rsteps * 2048));
+  const uint32_t t_so = __builtin_amdgcn_readfirstlane(t_block0 + 4u * wave * blk + (uint32_t)rs * 2048u);
+  const uint32_t lt = __builtin_amdgcn_readfirstlane(lds_stage_addr + wave * 8192u);
+  const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_stage_addr + kAStageOff + wave * 4096u);
+  const uint32_t vt = 16u * lane;
+  const int64_t j = 32 * rs + 8 * (lane >> 4);
+  uint32_t vb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t n = n0 + 16 * (4 * (int64_t)wave + i) + (lane & 15);
+    vb[i] = (n < N && j + 8 <= r) ? (uint32_t)((n * r + j) * 2) : kOobOffset;
+  }
+  uint32_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[lt0]\n\t"
+      "buffer_load_dwordx4 %[vt], %[tr], %[ts0] offen lds\n\t"
+      "s_mov_b32 m0, %[lt1]\n\t"
+      "buffer_load_dwordx4 %[vt], %[tr], %[ts1] offen lds\n\t"
+      "s_mov_b32 m0, %[lt2]\n\t"
+      "buffer_load_dwordx4 %[vt], %[tr], %[ts2] offen lds\n\t"
+      "s_mov_b32 m0, %[lt3]\n\t"
+      "buffer_load_dwordx4 %[vt], %[tr], %[ts3] offen lds\n\t"
+      "s_mov_b32 m0, %[lt4]\n\t"
+      "buffer_load_dwordx4 %[vt], %[tr], %[ts4] offen lds\n\t"
+      "s_mov_b32 m0, %[lt5]\n\t"
+      "buffer_load_dwordx4 %[vt], %[tr], %[ts5] offen lds\n\t"
+      "s_mov_b32 m0, %[lt6]\n\t"
+      "buffer_load_dwordx4 %[vt], %[tr], %[ts6] offen lds\n\t"
+      "s_mov_b32 m0, %[lt7]\n\t"
+      "buffer_load_dwordx4 %[vt], %[tr], %[ts7] offen lds\n\t"
+      "s_mov_b32 m0, %[lb0]\n\t"
+      "buffer_load_dwordx4 %[vb0], %[br], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[lb1]\n\t"
+      "buffer_load_dwordx4 %[vb1], %[br], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[lb2]\n\t"
+      "buffer_load_dwordx4 %[vb2], %[br], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[lb3]\n\t"
+      "buffer_load_dwordx4 %[vb3], %[br], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[lb2]\n\t"
+      "buffer_load_dwordx4 %[vb2], %[br], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[lb3]\n\t"
+      "buffer_load_dwordx4 %[vb3], %[br], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [vt] "v"(vt), [vb0] "v"(vb[0]), [vb1] "v"(vb[1]), [vb2] "v"(vb[2]), [vb3] "v"(vb[3]),
+        [tr] "s"(tr), [br] "s"(br),
+        [ts0] "s"(t_so), [ts1] "s"(t_so + 1024u), [ts2] "s"(t_so + blk), [ts3] "s"(t_so + blk + 1024u),
+        [ts4] "s"(t_so + 2u * blk), [ts5] "s"(t_so + 2u * blk + 1024u), [ts6] "s"(t_so + 3u * blk),
+        [ts7] "s"(t_so + 3u * blk + 1024u),
+        [lt0] "s"(lt), [lt1] "s"(lt + 1024u), [lt2] "s"(lt + 2048u), [lt3] "s"(lt + 3072u),
+        [lt4] "s"(lt + 4096u), [lt5] "s"(lt + 5120u), [lt6] "s"(lt + 6144u), [lt7] "s"(lt + 7168u),
+        [lb0] "s"(lb), [lb1] "s"(lb + 1024u), [lb2] "s"(lb + 2048u), [lb3] "s"(lb + 3072u)
+      : "memory");
+  (void)saved;
+}
+
+// Copies the workgroup's 256 per-token scales into LDS (one dword DMA per
+// thread).  1 vector-memory operation.
+__device__ __forceinline__ void dma_scale_asm(__amdgpu_buffer_rsrc_t sr, uint32_t row0_bytes,
+                                              uint32_t lds_scale_addr) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t so = __builtin_amdgcn_readfirstlane(row0_bytes + 256u * wave);
+  const uint32_t ls = __builtin_amdgcn_readfirstlane(lds_scale_addr + 256u * wave);
+  const uint32_t v = 4u * lane;
+  uint32_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[ls]\n\t"
+      "buffer_load_dword %[v], %[sr], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [v] "v"(v), [sr] "s"(sr), [so] "s"(so), [ls] "s"(ls)
+      : "memory");
+  (void)saved;
+}
+
+// RING: the LoRA-up runs as extra steps of the LDS ring (r % 8 == 0 and
+// 16-byte W rows).  Otherwise it runs after the k loop from global memory
+// (odd ranks, K % 8 == 4: shapes outside the fast path).
+template <int KM, bool RING>
 __global__ void __launch_bounds__(kGemmThreads, 1)
 sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi,
                    const float* __restrict__ s, const u32x4* __restrict__ tfrag,
                    const uint16_t* __restrict__ w, const uint16_t* __restrict__ lora_b,
                    int64_t M, int64_t N, int64_t K, int64_t r, int64_t kpairs,
                    int64_t rsteps, uint16_t* __restrict__ y) {
-  constexpr int kStages = 3;                                   // LDS ring, prefetch distance 2
-  __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
+  static_assert(!RING || KM != kAligned8, "the ring's uniform waits need 14 operations per step");
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
   const int wm = wave >> 1, wn = wave & 1;
@@ -95,6 +199,8 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   const int64_t n0 = tn * kTileN;
   const int64_t mb0 = (tm * kTileM + wm * kWaveM) / 16;   // first 16-token block of this wavefront
   const int64_t ksteps = 2 * kpairs;
+  const int64_t lsteps = RING && r > 0 ? rsteps : 0;
+  const int64_t total = ksteps + lsteps;
 
   f32x4 acc[kRB][kCB];
 #pragma unroll
@@ -102,62 +208,77 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
 #pragma unroll
     for (int j = 0; j < kCB; ++j) acc[i][j] = (f32x4){0, 0, 0, 0};
 
-  // Every operand of the main loop arrives by DMA into a 3-stage LDS ring,
-  // two k-steps ahead; nothing in the loop is a compiler-visible memory
-  // load, so the explicit vmcnt waits are exact.
+  // Every operand of the loop arrives by DMA into a 3-stage LDS ring, two
+  // steps ahead; nothing in the loop is a compiler-visible memory load, so
+  // the explicit vmcnt waits are exact.
   const int64_t mgroups = (tiles_m * kTileM) / 128;      // 8-block groups in the workspace
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(xv, mgroups * ksteps * 8192);
   const __amdgpu_buffer_rsrc_t ir = make_rsrc(xi, mgroups * ksteps * 1024);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, N * K * 2);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, tiles_m * kTileM * 4);
+  const __amdgpu_buffer_rsrc_t tr = make_rsrc(tfrag, tiles_m * 16 * rsteps * 2048);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(lora_b, N * r * 2);
   const uint32_t a_group0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 8192));
   const uint32_t i_group0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 1024));
   const uint32_t a_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 8192));
   const uint32_t i_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 1024));
+  const uint32_t t_block0 = __builtin_amdgcn_readfirstlane((uint32_t)(tm * 16 * rsteps * 2048));
   const WTileOffsets wo = w_tile_offsets(K, n0);
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(&lds[0]);
   constexpr int kWOps = KM == kAligned8 ? 4 * kWChunksPerThread : kWChunksPerThread;
   constexpr int kStepOps = kWOps + 6;
 
-  auto prefetch = [&](int64_t ks, auto stage_c) {
-    constexpr int b = decltype(stage_c)::value;
-    const uint32_t st = lds_base + b * kStageBytes;
-    dma_a_tile_asm(ar, ir, a_group0, i_group0, a_gstride, i_gstride, ks, st);
-    if constexpr (KM == kAligned8) dma_w_tile_dword(wr, N, K, n0, ks * kTileK, &lds[b * kStageBytes]);
-    else dma_w_tile_asm(wr, wo, K, ks * kTileK, st, KM == kAligned16);
+  // Copies of step g (a k-step below ksteps, a LoRA step after) into stage b.
+  auto prefetch = [&](int64_t g, int b) {
+    const uint32_t st = lds_base + (uint32_t)b * kStageBytes;
+    if (RING && g >= ksteps) {
+      dma_lora_tile_asm(tr, br, t_block0, rsteps, g - ksteps, N, r, n0, st);
+      return;
+    }
+    dma_a_tile_asm(ar, ir, a_group0, i_group0, a_gstride, i_gstride, g, st);
+    if constexpr (KM == kAligned8) dma_w_tile_dword(wr, N, K, n0, g * kTileK, &lds[b * kStageBytes]);
+    else dma_w_tile_asm(wr, wo, K, g * kTileK, st, KM == kAligned16);
   };
 
-  const char* b_base = &lds[0] + 16 * lane + wn * kCB * 2048;
+  const char* b_base0 = &lds[0] + wn * kCB * 2048 + frag_lane_offset(0);
+  const char* b_base1 = &lds[0] + wn * kCB * 2048 + frag_lane_offset(1);
   const char* a_base = &lds[0] + kAStageOff + 16 * lane + wm * 8192;
   const char* i_base = &lds[0] + kIStageOff + 16 * lane + wm * 1024;
 
-  // One k-step ks in stage b = ks % 3: wait until only step ks + 1's copies
+  // Top of step g in stage b = g % 3: wait until only step g + 1's copies
   // are in flight, barrier (stage b complete for every wave; every wave done
-  // with stage (b + 2) % 3), start the copies of step ks + 2, then the
-  // matrix work: 8 A fragments and their position fields from LDS, the W
-  // fragments one column block ahead, 64 structured-sparse MFMAs.  The
-  // position fields of row blocks 2j and 2j+1 share a 32-bit word (abid).
-  auto step = [&](int64_t ks, auto b_c) {
-    constexpr int b = decltype(b_c)::value;
+  // with stage (b + 2) % 3), start the copies of step g + 2 (the last step
+  // again near the end: a harmless copy into a free stage).
+  auto step_top = [&](int64_t g, int b) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<kStepOps>();
     barrier_no_fence();
-    const int64_t kn = ks + 2 < ksteps ? ks + 2 : ksteps - 1;
-    prefetch(kn, std::integral_constant<int, (b + 2) % kStages>{});
+    prefetch(g + 2 < total ? g + 2 : total - 1, (b + 2) % kStages);
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One k-step: 8 A fragments and their position fields from LDS, the W
+  // fragments (two 16-byte halves per lane, swizzled tile) one column block
+  // ahead, 64 structured-sparse MFMAs.  The
+  // position fields of row blocks 2j and 2j+1 share a 32-bit word (abid).
+  auto kstep = [&](int64_t ks, auto b_c) {
+    constexpr int b = decltype(b_c)::value;
+    step_top(ks, b);
     const u32x4 iw = *reinterpret_cast<const u32x4*>(i_base + b * kStageBytes);
     bf16x8 af[kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
       af[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_base + b * kStageBytes + rb * 1024));
-    const char* stage = b_base + b * kStageBytes;
-    u32x4 b0 = *reinterpret_cast<const u32x4*>(stage);
-    u32x4 b1 = *reinterpret_cast<const u32x4*>(stage + 1024);
+    const char* s0 = b_base0 + b * kStageBytes;
+    const char* s1 = b_base1 + b * kStageBytes;
+    u32x4 b0 = *reinterpret_cast<const u32x4*>(s0);
+    u32x4 b1 = *reinterpret_cast<const u32x4*>(s1);
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
       const bf16x16 bf = __builtin_bit_cast(bf16x16, (u32x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
       if (cb + 1 < kCB) {
-        b0 = *reinterpret_cast<const u32x4*>(stage + (cb + 1) * 2048);
-        b1 = *reinterpret_cast<const u32x4*>(stage + (cb + 1) * 2048 + 1024);
+        b0 = *reinterpret_cast<const u32x4*>(s0 + (cb + 1) * 2048);
+        b1 = *reinterpret_cast<const u32x4*>(s1 + (cb + 1) * 2048);
       }
 #pragma unroll
       for (int rb = 0; rb < kRB; rb += 2) {
@@ -167,36 +288,54 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     }
   };
 
-  prefetch(0, std::integral_constant<int, 0>{});
-  prefetch(ksteps > 1 ? 1 : 0, std::integral_constant<int, 1>{});
+  // One LoRA step: for each half (hi, lo) of alpha T / s, 8 row fragments
+  // and 8 B fragments from LDS, 64 dense MFMAs.
+  auto lstep = [&](int64_t g, int b) {
+    step_top(g, b);
+    const char* st = &lds[0] + b * kStageBytes + 16 * lane;
+    bf16x8 bfr[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+      bfr[cb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + kAStageOff + (wn * kCB + cb) * 1024));
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) {
+      bf16x8 ta[kRB];
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+        ta[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + ((wm * kRB + rb) * 2 + hl) * 1024));
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta[rb], bfr[cb], acc[rb][cb], 0, 0, 0);
+    }
+  };
+
+  // Prologue: the tile's scales, then steps 0 and 1 (ksteps >= 2 always).
+  dma_scale_asm(sr, (uint32_t)(tm * kTileM * 4), lds_base + kScaleOff);
+  prefetch(0, 0);
+  prefetch(1, 1);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   int64_t ks = 0;
   for (; ks + 3 <= ksteps; ks += 3) {
-    step(ks + 0, I0{});
-    step(ks + 1, I1{});
-    step(ks + 2, I2{});
+    kstep(ks + 0, I0{});
+    kstep(ks + 1, I1{});
+    kstep(ks + 2, I2{});
   }
-  if (ks < ksteps) step(ks, I0{});
-  if (ks + 1 < ksteps) step(ks + 1, I1{});
+  if (ks < ksteps) kstep(ks, I0{});
+  if (ks + 1 < ksteps) kstep(ks + 1, I1{});
+  if constexpr (RING) {
+    for (int64_t g = ksteps; g < total; ++g) lstep(g, (int)(g % kStages));
+  }
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
+  barrier_no_fence();                     // every wave is done with the ring
 
-  // Epilogue 1: per-token compensation scale on the fp32 accumulators.
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const int64_t mb = mb0 + rb;
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(s + mb * 16 + 4 * (lane >> 4));
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[rb][cb][i] *= sv[i];
-  }
-
-  // Epilogue 2: LoRA-up, (alpha T)_hi B^T + (alpha T)_lo B^T on dense MFMAs.
-  if (r > 0) {
-    for (int64_t rs = 0; rs < rsteps; ++rs) {
+  if constexpr (!RING) {
+    // LoRA-up from global memory: (alpha T / s)_hi B^T + (alpha T / s)_lo B^T.
+    for (int64_t rs = 0; r > 0 && rs < rsteps; ++rs) {
       bf16x8 bfr[kCB];
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
@@ -231,7 +370,19 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     }
   }
 
-  store_acc_bf16(acc, y, M, N, tm * kTileM + wm * kWaveM, n0 + wn * kWaveN);
+  // Per-token compensation scale on the fp32 accumulators.
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(&lds[kScaleOff] + (wm * kWaveM + 16 * rb + 4 * (lane >> 4)) * 4);
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[rb][cb][i] *= sv[i];
+  }
+
+  const int64_t m0 = tm * kTileM + wm * kWaveM;
+  if (N % 8 == 0) store_tile_via_lds(acc, lds, y, M, N, m0, n0 + wn * kWaveN);
+  else store_acc_bf16(acc, y, M, N, m0, n0 + wn * kWaveN);
 }
 
 }  // namespace
@@ -247,17 +398,20 @@ hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const ui
   const u32x4* t = reinterpret_cast<const u32x4*>(ws + L.off_t);
   const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
   const dim3 grid((unsigned)tiles), block(kGemmThreads);
+  const int64_t kpairs = L.kp / 128, rsteps = L.rp / 32;
   // The k loop runs over the padded K (a multiple of 128): full-K mode
   // needs K itself to be one.
-  if (K % 128 == 0)
-    sparse_gemm_kernel<kFullK><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r,
-                                                           L.kp / 128, L.rp / 32, y);
+  const bool ring = r % 8 == 0;
+  if (K % 128 == 0 && ring)
+    sparse_gemm_kernel<kFullK, true><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
+  else if (K % 128 == 0)
+    sparse_gemm_kernel<kFullK, false><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
+  else if (K % 8 == 0 && ring)
+    sparse_gemm_kernel<kAligned16, true><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
   else if (K % 8 == 0)
-    sparse_gemm_kernel<kAligned16><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r,
-                                                               L.kp / 128, L.rp / 32, y);
+    sparse_gemm_kernel<kAligned16, false><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
   else
-    sparse_gemm_kernel<kAligned8><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r,
-                                                              L.kp / 128, L.rp / 32, y);
+    sparse_gemm_kernel<kAligned8, false><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
   return hipGetLastError();
 }
 

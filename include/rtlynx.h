@@ -31,6 +31,10 @@
  *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronise.  Outputs must not alias inputs.
  *   - Every base pointer must be 16-byte aligned.
+ *   - The linear-layer entry points address every tensor and every workspace
+ *     region with 32-bit offsets: each of X, W, Y, A, B and the workspace
+ *     regions must be smaller than 2 GiB (2^31 bytes), else
+ *     RTL_ERR_BAD_SHAPE.  Larger token counts are processed in row chunks.
  *   - Arguments are validated before any HIP call; on error nothing is
  *     launched and nothing is written.  The library keeps no sticky error
  *     state: a failed call leaves it usable.
@@ -51,7 +55,7 @@ extern "C" {
 typedef enum {
   RTL_OK = 0,
   RTL_ERR_NULL_POINTER = 1,      /* a required pointer is NULL              */
-  RTL_ERR_BAD_SHAPE = 2,         /* negative size, K % 4 != 0, K == 0, ...  */
+  RTL_ERR_BAD_SHAPE = 2,         /* negative size, K % 4 != 0, K == 0, 2 GiB */
   RTL_ERR_MISALIGNED = 3,        /* a base pointer is not 16-byte aligned    */
   RTL_ERR_WORKSPACE = 4,         /* workspace missing or too small           */
   RTL_ERR_NO_DEVICE = 5,         /* no HIP device is visible                 */

@@ -66,7 +66,8 @@ def test_workspace_bytes():
     for m, k, r in [(1, 4, 0), (64, 256, 8), (4096, 3072, 64), (9216, 3072, 64), (300, 516, 24), (257, 1000, 5)]:
         assert rtl.sparse_linear_workspace_bytes(m, k, r) == expect(m, k, r)
     assert rtl.sparse_linear_workspace_bytes(0, 256, 8) == 0
-    for bad in [(-1, 256, 8), (64, 6, 8), (64, 0, 8), (64, 256, -1), (64, 256, 129), (64, 2, 0)]:
+    for bad in [(-1, 256, 8), (64, 6, 8), (64, 0, 8), (64, 256, -1), (64, 256, 129), (64, 2, 0),
+                (1, 1 << 29, 0), (1 << 22, 256, 0)]:
         assert rtl.sparse_linear_workspace_bytes(*bad) == 0
 
 
@@ -91,6 +92,9 @@ def _dl(x=P, w=P2, m=64, n=128, k=256, y=P3, stream=None):
     (dict(a=P3 + 8), MISAL), (dict(b=P4 + 8), MISAL),
     (dict(ws=None), WS), (dict(wsb=1024), WS), (dict(ws=WSP + 8), MISAL),
     (dict(m=0), OK), (dict(n=0), OK), (dict(m=0, x=None, y=None), OK),
+    # 32-bit buffer offsets: every tensor below 2 GiB
+    (dict(m=1 << 22, k=256), SHAPE), (dict(n=1 << 22, k=256), SHAPE), (dict(m=1 << 15, n=1 << 15), SHAPE),
+    (dict(m=1, n=1, k=1 << 30, r=0), SHAPE), (dict(n=1 << 24, r=64), SHAPE),
 ])
 def test_sparse_linear_rejects_invalid_arguments(kw, status):
     assert _sl(**kw) == status
@@ -144,6 +148,9 @@ def test_valid_calls_without_a_device_report_no_device():
     assert _sp(scale=None, flags=1) == NODEV
     assert _sl() == NODEV
     assert _dl() == NODEV
+    # just below the 2 GiB limit: Y and its last tile's padding rows = 2^31 - 2^18 bytes
+    assert _dl(m=(1 << 14) - 256, n=(1 << 16) - 8) == NODEV
+    assert _dl(m=1 << 14, n=1 << 16) == SHAPE
     # the library stays usable after errors
     assert _sl(k=6) == SHAPE
     assert _sl() == NODEV
@@ -171,6 +178,7 @@ def _ap(ws=WSP, wsb=BIG, w=P, b=P2, m=64, n=128, k=256, r=8, y=P3, stream=None):
     (dict(k=6), SHAPE), (dict(r=129), SHAPE), (dict(m=-2), SHAPE),
     (dict(x=None), NULLP), (dict(a=None), NULLP), (dict(x=P + 8), MISAL), (dict(a=P2 + 8), MISAL),
     (dict(ws=None), WS), (dict(wsb=16), WS), (dict(ws=WSP + 4), MISAL), (dict(m=0), OK),
+    (dict(m=1, k=1 << 29, r=0), SHAPE),        # X is 1 GiB, but the padded workspace is 128 GiB
 ])
 def test_prepare_rejects_invalid_arguments(kw, status):
     assert _pr(**kw) == status
@@ -181,6 +189,7 @@ def test_prepare_rejects_invalid_arguments(kw, status):
     (dict(w=None), NULLP), (dict(b=None), NULLP), (dict(y=None), NULLP),
     (dict(w=P + 8), MISAL), (dict(b=P2 + 8), MISAL), (dict(y=P3 + 2), MISAL),
     (dict(ws=None), WS), (dict(wsb=16), WS), (dict(m=0), OK), (dict(n=0), OK),
+    (dict(m=1 << 15, n=1 << 15), SHAPE), (dict(n=1 << 23), SHAPE),
 ])
 def test_apply_rejects_invalid_arguments(kw, status):
     assert _ap(**kw) == status
