@@ -32,7 +32,8 @@ COMMON = [
 # Per-source extra flags.  sparse_gemm: MFMA accumulators and operands in
 # the VGPR form -- with the default heuristic its 256-register accumulator
 # tile splits between VGPRs and AGPRs and values spill to scratch, whose
-# reloads (vector-memory operations) would drain the DMA pipeline.
+# reloads (vector-memory operations) would drain the DMA pipeline.  (The
+# dense kernel is faster in the default form.)
 EXTRA = {
     "sparse_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }

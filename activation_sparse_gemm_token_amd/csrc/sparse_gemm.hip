@@ -15,8 +15,6 @@
 // alpha T / s (pre-pass) against B, into the same accumulators.  The scale
 // is applied once to the fp32 accumulators, never folded into a bf16
 // operand, and the tile leaves through LDS as coalesced 16-byte stores.
-#include <type_traits>
-
 #include "gemm_common.hpp"
 #include "rtl_kernels.hpp"
 
@@ -261,8 +259,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   // fragments (two 16-byte halves per lane, swizzled tile) one column block
   // ahead, 64 structured-sparse MFMAs.  The
   // position fields of row blocks 2j and 2j+1 share a 32-bit word (abid).
-  auto kstep = [&](int64_t ks, auto b_c) {
-    constexpr int b = decltype(b_c)::value;
+  auto kstep = [&](int64_t ks, int b) {
     step_top(ks, b);
     const u32x4 iw = *reinterpret_cast<const u32x4*>(i_base + b * kStageBytes);
     bf16x8 af[kRB];
@@ -315,17 +312,15 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   dma_scale_asm(sr, (uint32_t)(tm * kTileM * 4), lds_base + kScaleOff);
   prefetch(0, 0);
   prefetch(1, 1);
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  int64_t ks = 0;
-  for (; ks + 3 <= ksteps; ks += 3) {
-    kstep(ks + 0, I0{});
-    kstep(ks + 1, I1{});
-    kstep(ks + 2, I2{});
+  // One step per iteration, the stage a runtime index: unrolled copies of
+  // the step get different accumulator registers from the register
+  // allocator, and the copies between them wait on the matrix pipeline.
+  int b = 0;
+#pragma nounroll
+  for (int64_t ks = 0; ks < ksteps; ++ks) {
+    kstep(ks, b);
+    b = b == kStages - 1 ? 0 : b + 1;
   }
-  if (ks < ksteps) kstep(ks, I0{});
-  if (ks + 1 < ksteps) kstep(ks + 1, I1{});
   if constexpr (RING) {
     for (int64_t g = ksteps; g < total; ++g) lstep(g, (int)(g % kStages));
   }
