@@ -18,18 +18,23 @@ namespace rtl {
 
 namespace {
 
+// 4 wavefronts (2 x 2), each 128 x 128 = 8 x 8 blocks of 16 x 16.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWaveM = 128, kWaveN = 128;
+constexpr int kRB = kWaveM / 16, kCB = kWaveN / 16;
+
 template <int KM>
-__global__ void __launch_bounds__(kGemmThreads, 1)
+__global__ void __launch_bounds__(kThreads, 1)
 dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                   int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y) {
   constexpr int kWStages = 3, kAStages = 2;
   // One LDS block: the W ring, then the A ring; the epilogue reuses all of it.
-  constexpr int kLdsBytes = (kWStages + kAStages) * kWTileBytes;
-  static_assert(kStoreLdsBytes <= kLdsBytes, "store staging must fit in the rings");
+  constexpr int kLdsBytes = (kWStages + kAStages) * kTileBytes;
+  static_assert(store_lds_bytes<kRB, kCB>(kWaves) <= kLdsBytes, "store staging must fit in the rings");
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   char* const lds_w = lds;
-  char* const lds_a = lds + kWStages * kWTileBytes;
-  const int lane = threadIdx.x & 63;
+  char* const lds_a = lds + kWStages * kTileBytes;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (N + kTileN - 1) / kTileN;
@@ -49,14 +54,14 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
   // past K are pointed out of range in the tail modes.
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, M * K * 2);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, N * K * 2);
-  const WTileOffsets xo = w_tile_offsets(K, m0);
-  const WTileOffsets wo = w_tile_offsets(K, n0);
+  const WTileOffsets xo = w_tile_offsets<kWaves>(K, m0);
+  const WTileOffsets wo = w_tile_offsets<kWaves>(K, n0);
   const uint32_t f0 = frag_lane_offset(0), f1 = frag_lane_offset(1);
   const char* b_base0 = lds_w + wn * kCB * 2048 + f0;
   const char* b_base1 = lds_w + wn * kCB * 2048 + f1;
   const char* a_base0 = lds_a + wm * kRB * 2048 + f0;
   const char* a_base1 = lds_a + wm * kRB * 2048 + f1;
-  constexpr int kTileOps = KM == kAligned8 ? 4 * kWChunksPerThread : kWChunksPerThread;
+  constexpr int kTileOps = KM == kAligned8 ? 128 / kWaves : 32 / kWaves;
 
   // Both tile copies are issued as inline-asm DMA blocks: no vector-memory
   // operation of the loop is visible to the compiler, so it inserts no
@@ -66,10 +71,10 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
   auto copy_tile = [&](__amdgpu_buffer_rsrc_t rs, const WTileOffsets& o, int64_t row0, int64_t rows,
                        int64_t ks, char* dst) {
     if constexpr (KM == kAligned8) {
-      dma_w_tile_dword(rs, rows, K, row0, ks * kTileK, dst);
+      dma_w_tile_dword<kWaves>(rs, rows, K, row0, ks * kTileK, dst);
     } else {
       const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(dst);
-      dma_w_tile_asm(rs, o, K, ks * kTileK, lds_addr, KM == kAligned16);
+      dma_w_tile_asm<kWaves>(rs, o, K, ks * kTileK, lds_addr, KM == kAligned16);
     }
   };
 
@@ -84,13 +89,13 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
     barrier_no_fence();
     const int64_t ka = ks + 1 < ksteps ? ks + 1 : ksteps - 1;
     const int64_t kw = ks + 2 < ksteps ? ks + 2 : ksteps - 1;
-    copy_tile(xr, xo, m0, M, ka, lds_a + (1 - ba) * kWTileBytes);
-    copy_tile(wr, wo, n0, N, kw, lds_w + (bw + 2) % kWStages * kWTileBytes);
+    copy_tile(xr, xo, m0, M, ka, lds_a + (1 - ba) * kTileBytes);
+    copy_tile(wr, wo, n0, N, kw, lds_w + (bw + 2) % kWStages * kTileBytes);
     __builtin_amdgcn_sched_barrier(0);
-    const char* bs0 = b_base0 + bw * kWTileBytes;
-    const char* bs1 = b_base1 + bw * kWTileBytes;
-    const char* as0 = a_base0 + ba * kWTileBytes;
-    const char* as1 = a_base1 + ba * kWTileBytes;
+    const char* bs0 = b_base0 + bw * kTileBytes;
+    const char* bs1 = b_base1 + bw * kTileBytes;
+    const char* as0 = a_base0 + ba * kTileBytes;
+    const char* as1 = a_base1 + ba * kTileBytes;
     bf16x8 af[2][kRB];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
@@ -117,7 +122,7 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
 
   copy_tile(wr, wo, n0, N, 0, lds_w);
   copy_tile(xr, xo, m0, M, 0, lds_a);
-  copy_tile(wr, wo, n0, N, ksteps > 1 ? 1 : 0, lds_w + kWTileBytes);
+  copy_tile(wr, wo, n0, N, ksteps > 1 ? 1 : 0, lds_w + kTileBytes);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -140,8 +145,8 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
   wait_vm<0>();
   barrier_no_fence();                     // every wave is done with the rings
 
-  if (N % 8 == 0) store_tile_via_lds(acc, lds, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
-  else store_acc_bf16(acc, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
+  if (N % 8 == 0) store_tile_via_lds<kRB, kCB>(acc, lds, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
+  else store_acc_bf16<kRB, kCB>(acc, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
 }
 
 }  // namespace
@@ -149,7 +154,7 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
 hipError_t launch_dense_gemm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                              int64_t K, uint16_t* y, hipStream_t stream) {
   const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
-  const dim3 grid((unsigned)tiles), block(kGemmThreads);
+  const dim3 grid((unsigned)tiles), block(kThreads);
   if (K % kTileK == 0) dense_gemm_kernel<kFullK><<<grid, block, 0, stream>>>(x, w, M, N, K, y);
   else if (K % 8 == 0) dense_gemm_kernel<kAligned16><<<grid, block, 0, stream>>>(x, w, M, N, K, y);
   else dense_gemm_kernel<kAligned8><<<grid, block, 0, stream>>>(x, w, M, N, K, y);

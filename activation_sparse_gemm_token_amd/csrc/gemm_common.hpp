@@ -1,14 +1,13 @@
 // Pieces shared by the structured-sparse and the dense GEMM kernels.
 //
-// Both kernels compute a 256 x 256 output tile per workgroup of 4
-// wavefronts (2 x 2, each 128 x 128 = 8 x 8 blocks of 16 x 16) and stream
-// the weight through LDS in 64-deep k-steps, double-buffered.  The LDS copy
-// of a W tile is stored in matrix-core operand order: for every 16-column
-// block and every 32-channel half of the k-step, 64 lanes x 16 bytes, where
-// lane l holds column l % 16, channels 8 (l / 16) + [0, 8).  That is the B
-// operand of v_mfma_f32_16x16x32_bf16 for one half, and the two halves
-// together form the B operand of v_smfmac_f32_16x16x64_bf16, so each
-// wavefront reads its operands with lane-contiguous 16-byte LDS reads.
+// Both kernels compute a 256 x 256 output tile per workgroup and stream
+// their operands through a ring of LDS stages in 64-deep k-steps, filled
+// by direct global -> LDS copies (buffer_load ... lds).  The dense kernel
+// runs 4 wavefronts of 128 x 128, the structured-sparse one 8 wavefronts of
+// 128 x 64 (two per SIMD: one wavefront alone cannot issue LDS reads fast
+// enough to feed the structured-sparse matrix core).  The helpers below are
+// templated on the number of wavefronts WAVES that share a tile copy and on
+// the wavefront's block counts RB x CB (16 x 16 blocks).
 #pragma once
 
 #include "rtl_common.hpp"
@@ -16,57 +15,35 @@
 namespace rtl {
 
 constexpr int kTileM = 256, kTileN = 256, kTileK = 64;
-constexpr int kGemmThreads = 256;
-constexpr int kWaveM = 128, kWaveN = 128;
-constexpr int kRB = kWaveM / 16, kCB = kWaveN / 16;          // 8 x 8 blocks per wavefront
-constexpr int kWTileBytes = kTileN * kTileK * 2;             // 32 KiB per stage
-constexpr int kWChunksPerThread = kWTileBytes / 16 / kGemmThreads;   // 8
+constexpr int kTileBytes = kTileN * kTileK * 2;              // one 256 x 64 bf16 tile: 32 KiB
 
-// W-tile copy.  Thread (wave v, lane l) moves chunk i: 16-column block
-// cb = 4 v + i / 2, half h = i % 2, column n0 + 16 cb + l % 16, channels
-// k0 + 32 h + 8 (l / 16) + [0, 8), to LDS byte offset (2 cb + h) * 1024 + 16 l,
-// so every LDS write and read is lane-contiguous.  Columns past N read row
-// N - 1 (their results are never stored); channels past K read as zero.
-//
-// The copy goes through registers: the global loads of step k+1 are issued
-// at the top of step k and written to LDS at its end, so the compiler's own
-// vmcnt tracking waits exactly for them.  (The direct global->LDS form makes
-// the compiler drain every outstanding load before the next LDS read, which
-// serialises a memory latency into each step.)
-// Buffer resource over a whole tensor (raw, stride 0): loads past
-// `bytes` return zeros instead of faulting.  Tensors hold fewer than 2^31
-// elements, so byte offsets fit the 32-bit offset fields.
+// Buffer resource over a whole tensor (raw, stride 0): loads past `bytes`
+// return zeros instead of faulting, stores there are dropped.  The host
+// keeps every tensor below 2 GiB, so sizes and offsets fit 32 bits.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
-
 // How channel tails are handled.  kFullK: every k-step lies inside K (no
 // guard, the common case); kAligned16: rows are 16-byte aligned and the last
-// k-step is partial (16-byte loads, guarded per chunk); kAligned8: K % 8 == 4,
-// rows are only 8-byte aligned (8-byte loads, guarded per group).
+// k-step is partial (16-byte copies, guarded per chunk); kAligned8: K % 8 ==
+// 4, rows are only 8-byte aligned (4-byte copies, guarded per pair).
 enum KMode { kFullK = 0, kAligned16 = 1, kAligned8 = 2 };
 
 // A 256-row x 64-channel bf16 tile in LDS (the W tile, and the X tile of
 // the dense kernel): row-major, 128 bytes per row, with the 16-byte chunk c
 // (channels 8c .. 8c + 7) of row n stored in slot c ^ (n & 7) of the row.
 // The copy then reads whole 128-byte lines of the row-major source (8 lanes
-// per row), and a fragment read -- 16 rows at one chunk index -- spreads over
-// all LDS banks.
+// per row), and a fragment read -- 16 rows at one chunk index -- spreads
+// over all LDS banks.
 //
-// Copy: instruction i of wavefront v moves rows 64 v + 8 i + [0, 8); lane l
-// fills LDS slot l % 8 of row l / 8 (the DMA writes lane l's 16 bytes to
-// M0 + 16 l) with source chunk (l % 8) ^ (l / 8).  Byte offsets (at channel
-// 0) are one per-lane base plus a uniform 8-row step, so one VGPR stays
-// live; rows past the end of the tensor lie past its end and read as zeros
-// (the row is in the VGPR offset, which the buffer range check covers).
+// Copy: wavefront v moves rows (256 / WAVES) v + [0, 256 / WAVES), 8 rows
+// per instruction; lane l fills LDS slot l % 8 of row l / 8 of its 8 (the
+// DMA writes lane l's 16 bytes to M0 + 16 l) with source chunk
+// (l % 8) ^ (l / 8).  Byte offsets (at channel 0) are one per-lane base
+// plus a uniform 8-row step, so one VGPR stays live; rows past the end of
+// the tensor lie past its end and read as zeros (the row is in the VGPR
+// offset, which the buffer range check covers).
 struct WTileOffsets {
   uint32_t base;                  // VGPR
   uint32_t row8;                  // uniform: bytes of 8 rows
@@ -74,11 +51,12 @@ struct WTileOffsets {
   __device__ __forceinline__ uint32_t off(int i) const { return base + (uint32_t)i * row8; }
 };
 
+template <int WAVES>
 __device__ __forceinline__ WTileOffsets w_tile_offsets(int64_t K, int64_t n0) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   WTileOffsets o;
   o.k_lane = 8 * ((lane & 7) ^ (lane >> 3));
-  o.base = (uint32_t)(((n0 + 64 * wave + (lane >> 3)) * K + o.k_lane) * 2);
+  o.base = (uint32_t)(((n0 + (256 / WAVES) * wave + (lane >> 3)) * K + o.k_lane) * 2);
   o.row8 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * K * 2));
   return o;
 }
@@ -96,81 +74,104 @@ __device__ __forceinline__ uint32_t frag_lane_offset(int h) {
 // Byte offset that lies past every tensor: a buffer load there returns zeros.
 constexpr uint32_t kOobOffset = 0xfffffff0u;
 
-// The tile copy at channel k0 (K % 8 == 0) as one inline-asm block of 8
-// buffer_load_dwordx4 ... lds instructions.  The compiler does not see these
-// loads, so it never inserts vmcnt waits for them (with the builtin it
-// sometimes cannot prove that a copy into one stage does not alias reads of
-// another, and drains all loads); the caller accounts for them with
-// explicit vmcnt waits.  The block has no output registers -- the data goes
-// to LDS -- and writes only M0, which it saves and restores; it uses no
-// instruction that sets SCC.  s_nop 4 covers a VALU write of an SGPR operand
-// right before the block.  With guard_k, chunks past K are pointed out of
-// the buffer and arrive as zeros.
+// The tile copy at channel k0 (K % 8 == 0) as one inline-asm block of
+// 32 / WAVES buffer_load_dwordx4 ... lds instructions.  The compiler does
+// not see these loads, so it never inserts vmcnt waits for them (with the
+// builtin it sometimes cannot prove that a copy into one stage does not
+// alias reads of another, and drains all loads); the caller accounts for
+// them with explicit vmcnt waits.  The block has no output registers -- the
+// data goes to LDS -- and writes only M0, which it saves and restores; it
+// uses no instruction that sets SCC.  s_nop 4 covers a VALU write of an
+// SGPR operand right before the block.  With guard_k, chunks past K are
+// pointed out of the buffer and arrive as zeros.
+template <int WAVES>
 __device__ __forceinline__ void dma_w_tile_asm(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
                                                int64_t k0, uint32_t lds_stage_addr, bool guard_k) {
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 wavefronts share a tile copy");
+  constexpr int NI = 32 / WAVES;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(k0 * 2));
   const bool chunk_ok = !guard_k || k0 + o.k_lane + 8 <= K;
-  uint32_t v[kWChunksPerThread];
+  uint32_t v[NI];
 #pragma unroll
-  for (int i = 0; i < kWChunksPerThread; ++i) v[i] = chunk_ok ? o.off(i) : kOobOffset - soff;
-  // LDS byte address of instruction i: stage + 128 (64 wave + 8 i) =
-  // stage + 8192 wave + 1024 i.  All eight are computed outside the block,
-  // which then only moves them into M0 (s_mov does not touch SCC).
-  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_stage_addr + 8192u * (uint32_t)wave);
+  for (int i = 0; i < NI; ++i) v[i] = chunk_ok ? o.off(i) : kOobOffset - soff;
+  // LDS byte address of instruction i: stage + 128 ((256 / WAVES) wave + 8 i).
+  // All are computed outside the block, which then only moves them into M0
+  // (s_mov does not touch SCC).
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_stage_addr + 128u * (256 / WAVES) * (uint32_t)wave);
   uint32_t saved;
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[l0]\n\t"
-      "buffer_load_dwordx4 %[v0], %[rs], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[l1]\n\t"
-      "buffer_load_dwordx4 %[v1], %[rs], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[l2]\n\t"
-      "buffer_load_dwordx4 %[v2], %[rs], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[l3]\n\t"
-      "buffer_load_dwordx4 %[v3], %[rs], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[l4]\n\t"
-      "buffer_load_dwordx4 %[v4], %[rs], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[l5]\n\t"
-      "buffer_load_dwordx4 %[v5], %[rs], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[l6]\n\t"
-      "buffer_load_dwordx4 %[v6], %[rs], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[l7]\n\t"
-      "buffer_load_dwordx4 %[v7], %[rs], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [v4] "v"(v[4]), [v5] "v"(v[5]),
-        [v6] "v"(v[6]), [v7] "v"(v[7]), [rs] "s"(wr), [so] "s"(soff), [l0] "s"(l0), [l1] "s"(l0 + 0x400u),
-        [l2] "s"(l0 + 0x800u), [l3] "s"(l0 + 0xc00u), [l4] "s"(l0 + 0x1000u), [l5] "s"(l0 + 0x1400u),
-        [l6] "s"(l0 + 0x1800u), [l7] "s"(l0 + 0x1c00u)
-      : "memory");
+  if constexpr (NI == 8) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[l0]\n\t"
+        "buffer_load_dwordx4 %[v0], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l1]\n\t"
+        "buffer_load_dwordx4 %[v1], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l2]\n\t"
+        "buffer_load_dwordx4 %[v2], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l3]\n\t"
+        "buffer_load_dwordx4 %[v3], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l4]\n\t"
+        "buffer_load_dwordx4 %[v4], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l5]\n\t"
+        "buffer_load_dwordx4 %[v5], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l6]\n\t"
+        "buffer_load_dwordx4 %[v6], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l7]\n\t"
+        "buffer_load_dwordx4 %[v7], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [v4] "v"(v[4]), [v5] "v"(v[5]),
+          [v6] "v"(v[6]), [v7] "v"(v[7]), [rs] "s"(wr), [so] "s"(soff), [l0] "s"(l0), [l1] "s"(l0 + 0x400u),
+          [l2] "s"(l0 + 0x800u), [l3] "s"(l0 + 0xc00u), [l4] "s"(l0 + 0x1000u), [l5] "s"(l0 + 0x1400u),
+          [l6] "s"(l0 + 0x1800u), [l7] "s"(l0 + 0x1c00u)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[l0]\n\t"
+        "buffer_load_dwordx4 %[v0], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l1]\n\t"
+        "buffer_load_dwordx4 %[v1], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l2]\n\t"
+        "buffer_load_dwordx4 %[v2], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[l3]\n\t"
+        "buffer_load_dwordx4 %[v3], %[rs], %[so] offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [rs] "s"(wr), [so] "s"(soff),
+          [l0] "s"(l0), [l1] "s"(l0 + 0x400u), [l2] "s"(l0 + 0x800u), [l3] "s"(l0 + 0xc00u)
+        : "memory");
+  }
   (void)saved;
 }
 
-// Tile copy for K % 8 == 4 (rows only 8-byte aligned): 32 dword DMAs per
-// thread through the builtin, which the compiler tracks (and drains before
-// later LDS reads -- slow, but this mode only serves odd channel counts).
-// Instruction b of wavefront v fills rows 64 v + 2 b + [0, 2); DMA lane j
-// writes dword j % 4 of slot (j % 32) / 4 of row j / 32, so the LDS layout
-// matches the 16-byte copy.
+// Tile copy for K % 8 == 4 (rows only 8-byte aligned): 128 / WAVES dword
+// DMAs per thread through the builtin, which the compiler tracks (and
+// drains before later LDS reads -- slow, but this mode only serves odd
+// channel counts).  Instruction b of wavefront v fills rows
+// (256 / WAVES) v + 2 b + [0, 2); DMA lane j writes dword j % 4 of slot
+// (j % 32) / 4 of row j / 32, so the LDS layout matches the 16-byte copy.
+template <int WAVES>
 __device__ __forceinline__ void dma_w_tile_dword(__amdgpu_buffer_rsrc_t wr, int64_t N, int64_t K, int64_t n0,
                                                  int64_t k0, char* lds_stage) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int b = 0; b < 32; ++b) {
-    const int row = 64 * wave + 2 * b + (lane >> 5);
+  for (int b = 0; b < 128 / WAVES; ++b) {
+    const int row = (256 / WAVES) * wave + 2 * b + (lane >> 5);
     const int chunk = ((lane & 31) >> 2) ^ (row & 7);
     const int64_t n = n0 + row;
     const int64_t k = k0 + 8 * chunk + 2 * (lane & 3);
     const uint32_t voff = (k + 2 <= K && n < N) ? (uint32_t)((n * K + k) * 2) : kOobOffset;
-    char* dst = lds_stage + (64 * wave + 2 * b) * 128;
+    char* dst = lds_stage + ((256 / WAVES) * wave + 2 * b) * 128;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(dst), 4, voff, 0, 0, 0);
   }
 }
 
 // Workgroup barrier without the release fence of __syncthreads(), whose
-// "vmcnt(0)" would also drain the W copies of later stages still in flight.
+// "vmcnt(0)" would also drain the copies of later stages still in flight.
 // The asm statement is a full compiler memory barrier; the caller waits
 // explicitly for the data the barrier publishes.
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
@@ -206,14 +207,16 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   tn = first_n + in % gw;
 }
 
-// Stores a wavefront's 128 x 128 fp32 accumulators as bf16.
-__device__ __forceinline__ void store_acc_bf16(const f32x4 (&acc)[kRB][kCB], uint16_t* __restrict__ y,
+// Stores a wavefront's (16 RB) x (16 CB) fp32 accumulators as bf16, one
+// element per lane and store (any N).
+template <int RB, int CB>
+__device__ __forceinline__ void store_acc_bf16(const f32x4 (&acc)[RB][CB], uint16_t* __restrict__ y,
                                                int64_t M, int64_t N, int64_t m0, int64_t n0) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       const int64_t n = n0 + 16 * cb + (lane & 15);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -224,47 +227,53 @@ __device__ __forceinline__ void store_acc_bf16(const f32x4 (&acc)[kRB][kCB], uin
   }
 }
 
-// Epilogue store through LDS.  Each wavefront writes its 128 x 128 tile
-// as bf16 into its own LDS region (row pitch 272 bytes: 16-byte aligned
-// rows, and the four row groups of one write are 16 banks apart), then reads it back 16 bytes
-// per lane along rows and issues 32 coalesced 16-byte buffer stores (4 rows
-// x 256 bytes each) instead of 256 scattered 2-byte stores.  The caller
-// must have drained every DMA and passed a barrier, so that the LDS ring is
-// free (4 x 34 KiB).  Requires N % 8 == 0 (a chunk of 8 columns is all
-// inside or all outside Y); chunks past M or N are pointed out of range,
-// and the whole offset is in the VGPR operand.
-constexpr int kStorePitch = 272;
-constexpr int kStoreRegion = kWaveM * kStorePitch;      // 34 KiB per wavefront
-constexpr int kStoreLdsBytes = 4 * kStoreRegion;
+// Epilogue store through LDS.  Each wavefront writes its (16 RB) x (16 CB)
+// tile as bf16 into its own LDS region (row pitch 32 CB + 16 bytes: 16-byte
+// aligned rows, and the four row groups of one write fall on different
+// banks), then reads it back 16 bytes per lane along rows and issues
+// coalesced 16-byte buffer stores (whole rows of the tile) instead of
+// scattered 2-byte stores.  The caller must have drained every copy and
+// passed a barrier, so that the LDS ring is free (store_lds_bytes).
+// Requires N % 8 == 0 (a chunk of 8 columns is all inside or all outside
+// Y); chunks past M or N are pointed out of range, and the whole offset is
+// in the VGPR operand.
+template <int CB>
+constexpr int store_pitch() { return 32 * CB + 16; }
 
-__device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[kRB][kCB], char* lds_base,
+template <int RB, int CB>
+constexpr int store_lds_bytes(int waves) { return waves * 16 * RB * store_pitch<CB>(); }
+
+template <int RB, int CB>
+__device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[RB][CB], char* lds_base,
                                                    uint16_t* __restrict__ y, int64_t M, int64_t N,
                                                    int64_t m0, int64_t n0) {
+  constexpr int kPitch = store_pitch<CB>();
+  constexpr int kChunks = 2 * CB;                  // 16-byte chunks per row
+  constexpr int kRowsPerPass = 64 / kChunks;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  char* region = lds_base + wave * kStoreRegion;
+  char* region = lds_base + wave * 16 * RB * kPitch;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * rb + 4 * (lane >> 4) + i, col = 16 * cb + (lane & 15);
-        *reinterpret_cast<uint16_t*>(region + row * kStorePitch + 2 * col) =
-            (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
+        *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * col) = (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
       }
   // Only this wavefront reads its region back: a wave-local LDS wait suffices.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, M * N * 2);
-  const int sub_row = lane >> 4, chunk = lane & 15;        // 4 rows x 16 chunks of 8 columns
+  const int sub_row = lane / kChunks, chunk = lane % kChunks;
   const int64_t col = n0 + 8 * chunk;
   const bool col_ok = col + 8 <= N;
   const uint32_t lane_off = (uint32_t)(((m0 + sub_row) * N + col) * 2);
-  const uint32_t row4 = (uint32_t)(4 * N * 2);
+  const uint32_t pass_bytes = (uint32_t)(kRowsPerPass * N * 2);
 #pragma unroll
-  for (int it = 0; it < kWaveM / 4; ++it) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(region + (4 * it + sub_row) * kStorePitch + 16 * chunk);
-    const bool ok = col_ok && m0 + 4 * it + sub_row < M;
-    const uint32_t voff = ok ? lane_off + (uint32_t)it * row4 : kOobOffset;
+  for (int it = 0; it < 16 * RB / kRowsPerPass; ++it) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region + (kRowsPerPass * it + sub_row) * kPitch + 16 * chunk);
+    const bool ok = col_ok && m0 + kRowsPerPass * it + sub_row < M;
+    const uint32_t voff = ok ? lane_off + (uint32_t)it * pass_bytes : kOobOffset;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), yr,
                                            voff, 0, 0);
   }

@@ -37,11 +37,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The sources that make up the structured-sparse GEMM kernel (its code and
+# the workspace layout it reads).
+GEMM_SOURCES = ("sparse_gemm.hip", "gemm_common.hpp", "rtl_common.hpp", "rtl_kernels.hpp")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: counter readings are only reported for the
-    kernels they were taken on."""
+    """Hash of the GEMM kernel's sources: counter readings are only reported
+    for the kernel they were taken on."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in GEMM_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
@@ -132,7 +137,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="mlp_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=8)
     ap.add_argument("--counters", action="store_true",
                     help="a short launch sequence for rocprofv3 --pmc passes: 3 x (prepare, apply, dense, "
                          "sparsify) and 3 plain 256 MiB copies (the calibration kernel); prints no JSON")
