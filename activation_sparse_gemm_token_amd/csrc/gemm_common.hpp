@@ -17,13 +17,6 @@ namespace rtl {
 constexpr int kTileM = 256, kTileN = 256, kTileK = 64;
 constexpr int kTileBytes = kTileN * kTileK * 2;              // one 256 x 64 bf16 tile: 32 KiB
 
-// Buffer resource over a whole tensor (raw, stride 0): loads past `bytes`
-// return zeros instead of faulting, stores there are dropped.  The host
-// keeps every tensor below 2 GiB, so sizes and offsets fit 32 bits.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // How channel tails are handled.  kFullK: every k-step lies inside K (no
 // guard, the common case); kAligned16: rows are 16-byte aligned and the last
 // k-step is partial (16-byte copies, guarded per chunk); kAligned8: K % 8 ==
@@ -70,9 +63,6 @@ __device__ __forceinline__ uint32_t frag_lane_offset(int h) {
   const int lane = threadIdx.x & 63;
   return (uint32_t)((lane & 15) * 128 + (((4 * h + (lane >> 4)) ^ (lane & 7)) << 4));
 }
-
-// Byte offset that lies past every tensor: a buffer load there returns zeros.
-constexpr uint32_t kOobOffset = 0xfffffff0u;
 
 // The tile copy at channel k0 (K % 8 == 0) as one inline-asm block of
 // 32 / WAVES buffer_load_dwordx4 ... lds instructions.  The compiler does

@@ -62,27 +62,27 @@ __device__ __forceinline__ void select_quad(const uint32_t (&w)[8], Quad& q, flo
   }
 }
 
+// The loads below go through buffer resources: a guarded element is given
+// an offset past the end of the tensor and reads as zero, so no load sits
+// behind a branch and the compiler can issue them all before waiting.
+
+// 16 channels k .. k + 15 of one row of X.
 template <bool ALIGNED16>
-__device__ __forceinline__ void load_quad(const uint16_t* __restrict__ row_ptr, bool row_ok,
+__device__ __forceinline__ void load_quad(__amdgpu_buffer_rsrc_t xr, int64_t row, bool row_ok,
                                           int64_t k, int64_t K, uint32_t (&w)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = 0;
-  if (!row_ok) return;
   if constexpr (ALIGNED16) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      if (k + 8 * h + 8 <= K) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(row_ptr + k + 8 * h);
-        w[4 * h + 0] = v[0]; w[4 * h + 1] = v[1]; w[4 * h + 2] = v[2]; w[4 * h + 3] = v[3];
-      }
+      const bool ok = row_ok && k + 8 * h + 8 <= K;
+      const u32x4 v = buf_load16(xr, ok ? (uint32_t)((row * K + k + 8 * h) * 2) : kOobOffset);
+      w[4 * h + 0] = v[0]; w[4 * h + 1] = v[1]; w[4 * h + 2] = v[2]; w[4 * h + 3] = v[3];
     }
   } else {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if (k + 4 * g + 4 <= K) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(row_ptr + k + 4 * g);
-        w[2 * g] = v[0]; w[2 * g + 1] = v[1];
-      }
+      const bool ok = row_ok && k + 4 * g + 4 <= K;
+      const u32x2 v = buf_load8(xr, ok ? (uint32_t)((row * K + k + 4 * g) * 2) : kOobOffset);
+      w[2 * g] = v[0]; w[2 * g + 1] = v[1];
     }
   }
 }
@@ -91,27 +91,22 @@ __device__ __forceinline__ void load_quad(const uint16_t* __restrict__ row_ptr, 
 // matrix: lane l takes row n = n0 + l % 16 and the channels
 // k0 + 8 (l / 16) + [0, 8) and k0 + 32 + 8 (l / 16) + [0, 8).
 template <bool ALIGNED16>
-__device__ __forceinline__ bf16x16 load_b_sparse(const uint16_t* __restrict__ base, int64_t rows,
-                                                 int64_t K, int64_t n, int64_t k0, int lane) {
-  u32x8 v = (u32x8){0, 0, 0, 0, 0, 0, 0, 0};
-  if (n < rows) {
-    const uint16_t* p = base + n * K;
+__device__ __forceinline__ bf16x16 load_b_sparse(__amdgpu_buffer_rsrc_t br, int64_t rows, int64_t K,
+                                                 int64_t n, int64_t k0, int lane) {
+  u32x8 v;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t k = k0 + 32 * h + 8 * (lane >> 4);
-      if constexpr (ALIGNED16) {
-        if (k + 8 <= K) {
-          const u32x4 c = *reinterpret_cast<const u32x4*>(p + k);
-          v[4 * h + 0] = c[0]; v[4 * h + 1] = c[1]; v[4 * h + 2] = c[2]; v[4 * h + 3] = c[3];
-        }
-      } else {
+  for (int h = 0; h < 2; ++h) {
+    const int64_t k = k0 + 32 * h + 8 * (lane >> 4);
+    if constexpr (ALIGNED16) {
+      const bool ok = n < rows && k + 8 <= K;
+      const u32x4 c = buf_load16(br, ok ? (uint32_t)((n * K + k) * 2) : kOobOffset);
+      v[4 * h + 0] = c[0]; v[4 * h + 1] = c[1]; v[4 * h + 2] = c[2]; v[4 * h + 3] = c[3];
+    } else {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          if (k + 4 * q + 4 <= K) {
-            const u32x2 c = *reinterpret_cast<const u32x2*>(p + k + 4 * q);
-            v[4 * h + 2 * q] = c[0]; v[4 * h + 2 * q + 1] = c[1];
-          }
-        }
+      for (int q = 0; q < 2; ++q) {
+        const bool ok = n < rows && k + 4 * q + 4 <= K;
+        const u32x2 c = buf_load8(br, ok ? (uint32_t)((n * K + k + 4 * q) * 2) : kOobOffset);
+        v[4 * h + 2 * q] = c[0]; v[4 * h + 2 * q + 1] = c[1];
       }
     }
   }
@@ -132,10 +127,20 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t mb = blockIdx.x;
+  // Block mapping: the 8 16-token blocks of a group share 16-byte chunks of
+  // the position-field array (2 bytes each), so they are processed on one
+  // XCD (workgroup i runs on XCD i % 8), whose L2 merges the partial writes
+  // before they reach memory.  Group g runs on XCD g % 8; padding
+  // workgroups past the last group exit at once.
+  const int64_t ngroups = 2 * ((M + 255) / 256);       // padded rows / 128
+  const int64_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  const int64_t grp_id = 8 * (local / 8) + xcd;
+  if (grp_id >= ngroups) return;
+  const int64_t mb = 8 * grp_id + local % 8;
   const int64_t row = mb * 16 + (lane & 15);
   const bool row_ok = row < M;
-  const uint16_t* row_ptr = x + (row_ok ? row : 0) * K;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, M * K * 2);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(lora_a, r * K * 2);
   const int64_t ksteps = 2 * kpairs;
 
   float lk = 0.f, lp = 0.f;
@@ -145,14 +150,40 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
 
   const int64_t p_begin = (int64_t)wave * kpairs / kWaves;
   const int64_t p_end = (int64_t)(wave + 1) * kpairs / kWaves;
+  // Software pipeline over the wavefront's k-pairs: the loads of k-pair
+  // p + 1 (X and the LoRA A operand) are in flight while k-pair p is
+  // selected, compressed and multiplied.
+  uint32_t w0[8], w1[8];
+  bf16x16 bA[NT][2];
+  auto load_pair = [&](int64_t p) {
+    const int64_t k = 128 * p + 16 * (lane >> 4);
+    load_quad<ALIGNED16>(xr, row, row_ok, k, K, w0);
+    load_quad<ALIGNED16>(xr, row, row_ok, k + 64, K, w1);
+    if constexpr (NCB > 0) {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const int64_t n = c * 16 + (lane & 15);
+        bA[c][0] = load_b_sparse<ALIGNED16>(ar, r, K, n, 128 * p, lane);
+        bA[c][1] = load_b_sparse<ALIGNED16>(ar, r, K, n, 128 * p + 64, lane);
+      }
+    }
+  };
+  if (p_begin < p_end) load_pair(p_begin);
   for (int64_t p = p_begin; p < p_end; ++p) {
-    uint32_t w0[8], w1[8];
+    uint32_t x0[8], x1[8];
+    bf16x16 b[NT][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { x0[i] = w0[i]; x1[i] = w1[i]; }
+    if constexpr (NCB > 0) {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) { b[c][0] = bA[c][0]; b[c][1] = bA[c][1]; }
+    }
+    if (p + 1 < p_end) load_pair(p + 1);
+    __builtin_amdgcn_sched_barrier(0);
     const int64_t ks0 = 2 * p;
-    load_quad<ALIGNED16>(row_ptr, row_ok, ks0 * 64 + 16 * (lane >> 4), K, w0);
-    load_quad<ALIGNED16>(row_ptr, row_ok, ks0 * 64 + 64 + 16 * (lane >> 4), K, w1);
     Quad q0, q1;
-    select_quad(w0, q0, lk, lp);
-    select_quad(w1, q1, lk, lp);
+    select_quad(x0, q0, lk, lp);
+    select_quad(x1, q1, lk, lp);
     const int64_t grp = mb >> 3, sub = mb & 7;
     xv[((grp * ksteps + ks0) * 8 + sub) * 64 + lane] = q0.kept;
     xv[((grp * ksteps + ks0 + 1) * 8 + sub) * 64 + lane] = q1.kept;
@@ -161,13 +192,10 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
     if constexpr (NCB > 0) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
-        const int64_t n = c * 16 + (lane & 15);
-        const bf16x16 b0 = load_b_sparse<ALIGNED16>(lora_a, r, K, n, ks0 * 64, lane);
-        const bf16x16 b1 = load_b_sparse<ALIGNED16>(lora_a, r, K, n, ks0 * 64 + 64, lane);
-        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.kept), b0, tk[c], (int)q0.kcode, 0, 0);
-        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.pruned), b0, tp[c], (int)q0.pcode, 0, 0);
-        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.kept), b1, tk[c], (int)q1.kcode, 0, 0);
-        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.pruned), b1, tp[c], (int)q1.pcode, 0, 0);
+        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.kept), b[c][0], tk[c], (int)q0.kcode, 0, 0);
+        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.pruned), b[c][0], tp[c], (int)q0.pcode, 0, 0);
+        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.kept), b[c][1], tk[c], (int)q1.kcode, 0, 0);
+        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.pruned), b[c][1], tp[c], (int)q1.pcode, 0, 0);
       }
     }
   }
@@ -232,7 +260,10 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
 template <bool A16>
 hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M, int64_t K,
                             int64_t r, float alpha, const WsLayout& L, char* ws, hipStream_t stream) {
-  const dim3 grid((unsigned)(L.mp / 16)), block(64 * kWaves);
+  // 8 workgroups per group of 8 16-token blocks, groups rounded up to a
+  // multiple of 8 (the kernel's XCD-grouped mapping).
+  const int64_t ngroups = L.mp / 128;
+  const dim3 grid((unsigned)(64 * ((ngroups + 7) / 8))), block(64 * kWaves);
   u32x4* xv = reinterpret_cast<u32x4*>(ws + L.off_xv);
   uint16_t* xi = reinterpret_cast<uint16_t*>(ws + L.off_xi);
   float* s = reinterpret_cast<float*>(ws + L.off_s);

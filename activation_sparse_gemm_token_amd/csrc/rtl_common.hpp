@@ -124,4 +124,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// Buffer resource over a whole tensor (raw, stride 0): loads past `bytes`
+// return zeros instead of faulting, stores there are dropped.  The host
+// keeps every tensor below 2 GiB, so sizes and offsets fit 32 bits.  Guarded
+// loads through it need no branch: an out-of-range element gets an offset
+// past the end (kOobOffset) and reads as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Byte offset that lies past every tensor: a buffer load there returns zeros.
+constexpr uint32_t kOobOffset = 0xfffffff0u;
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+}
+
 }  // namespace rtl
