@@ -182,9 +182,11 @@ __device__ __forceinline__ void wait_vm() {
 constexpr int kXcds = 8;
 constexpr int kGroupN = 4;
 
-__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+// Tile of ordinal `id` (the workgroup id, or a persistent workgroup's
+// virtual id blockIdx.x + i * gridDim.x, which runs on the same XCD).
+__device__ __forceinline__ void tile_coords_of(int64_t id, int64_t tiles_m, int64_t tiles_n, int64_t& tm,
+                                               int64_t& tn) {
   const int64_t total = tiles_m * tiles_n;
-  const int64_t id = blockIdx.x;
   const int64_t xcd = id % kXcds, local = id / kXcds;
   const int64_t per = total / kXcds, extra = total % kXcds;
   const int64_t lin = xcd * per + (xcd < extra ? xcd : extra) + local;   // bijection on [0, total)
@@ -195,6 +197,10 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   const int64_t in = lin - g * per_group;
   tm = in / gw;
   tn = first_n + in % gw;
+}
+
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  tile_coords_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
 }
 
 // Stores a wavefront's (16 RB) x (16 CB) fp32 accumulators as bf16, one
@@ -266,6 +272,57 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[RB][CB], c
     const uint32_t voff = ok ? lane_off + (uint32_t)it * pass_bytes : kOobOffset;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), yr,
                                            voff, 0, 0);
+  }
+}
+
+// Vector-memory operations (buffer stores) store_tile_via_lds_passes
+// issues per wavefront.
+template <int RB, int CB, int PRB>
+constexpr int store_passes_ops() { return (RB / PRB) * (16 * PRB / (64 / (2 * CB))); }
+
+// The same store in passes of PRB row blocks through a smaller region
+// (16 PRB rows x store_pitch<CB>() bytes per wavefront at `region`), for a
+// persistent kernel whose ring keeps the next tile's copies in flight.
+template <int RB, int CB, int PRB>
+__device__ __forceinline__ void store_tile_via_lds_passes(const f32x4 (&acc)[RB][CB], char* region,
+                                                          uint16_t* __restrict__ y, int64_t M, int64_t N,
+                                                          int64_t m0, int64_t n0) {
+  static_assert(RB % PRB == 0, "whole passes");
+  constexpr int kPitch = store_pitch<CB>();
+  constexpr int kChunks = 2 * CB;                  // 16-byte chunks per row
+  constexpr int kRowsPerPass = 64 / kChunks;
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, M * N * 2);
+  const int sub_row = lane / kChunks, chunk = lane % kChunks;
+  const int64_t col = n0 + 8 * chunk;
+  const bool col_ok = col + 8 <= N;
+  const uint32_t pass_bytes = (uint32_t)(kRowsPerPass * N * 2);
+#pragma unroll
+  for (int pass = 0; pass < RB / PRB; ++pass) {
+#pragma unroll
+    for (int rr = 0; rr < PRB; ++rr)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rr + 4 * (lane >> 4) + i, c = 16 * cb + (lane & 15);
+          *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * c) =
+              (uint16_t)f32_to_bf16_rne(acc[pass * PRB + rr][cb][i]);
+        }
+    // Only this wavefront reads its region back; LDS operations of one
+    // wavefront execute in order, so the next pass's writes cannot overtake
+    // these reads.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int64_t mp = m0 + 16 * PRB * pass;
+    const uint32_t lane_off = (uint32_t)(((mp + sub_row) * N + col) * 2);
+#pragma unroll
+    for (int it = 0; it < 16 * PRB / kRowsPerPass; ++it) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + (kRowsPerPass * it + sub_row) * kPitch + 16 * chunk);
+      const bool ok = col_ok && mp + kRowsPerPass * it + sub_row < M;
+      const uint32_t voff = ok ? lane_off + (uint32_t)it * pass_bytes : kOobOffset;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v),
+                                             yr, voff, 0, 0);
+    }
   }
 }
 

@@ -23,6 +23,7 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int kMaxDevices = 64;
 
 std::atomic<int> g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cus[kMaxDevices];       // compute units of a known device
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -51,7 +52,8 @@ bool layer_sizes_ok(int64_t M, int64_t N, int64_t K, int64_t r) {
   return bytes_ok(L.mp, L.kp, 1) && bytes_ok(L.mp, L.rp, 4);
 }
 
-rtl_status check_device() {
+// Checks that a gfx950 device is current; sets *cus to its CU count.
+rtl_status check_device(int* cus = nullptr) {
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
     (void)hipGetLastError();
@@ -71,8 +73,10 @@ rtl_status check_device() {
       return RTL_ERR_HIP;
     }
     known = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_arch_ok[dev].store(known, std::memory_order_relaxed);
   }
+  if (cus != nullptr) *cus = g_cus[dev].load(std::memory_order_relaxed);
   return known == 1 ? RTL_OK : RTL_ERR_UNSUPPORTED_ARCH;
 }
 
@@ -129,9 +133,10 @@ RTL_API rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspa
   if (!aligned16(w) || !aligned16(y) || (r > 0 && !aligned16(lora_b))) return RTL_ERR_MISALIGNED;
   if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
-  const rtl_status d = check_device();
+  int cus = 0;
+  const rtl_status d = check_device(&cus);
   if (d != RTL_OK) return d;
-  return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y,
+  return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y, cus,
                                           static_cast<hipStream_t>(hip_stream)));
 }
 
@@ -148,12 +153,13 @@ RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const
   if (r > 0 && (!aligned16(lora_a) || !aligned16(lora_b))) return RTL_ERR_MISALIGNED;
   if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
-  const rtl_status d = check_device();
+  int cus = 0;
+  const rtl_status d = check_device(&cus);
   if (d != RTL_OK) return d;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (rtl::launch_prepass(x, r > 0 ? lora_a : nullptr, M, K, r, lora_scale, workspace, stream) != hipSuccess)
     return RTL_ERR_HIP;
-  return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y, stream));
+  return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y, cus, stream));
 }
 
 RTL_API rtl_status rtl_dense_linear(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,

@@ -41,9 +41,9 @@ constexpr int kAStageOff = kTileBytes;
 constexpr int kIStageOff = kTileBytes + 16 * 1024;
 constexpr int kStageBytes = kTileBytes + 18 * 1024;
 constexpr int kStages = 3;                                   // prefetch distance 2
-constexpr int kScaleOff = kStages * kStageBytes;             // 256 per-token scales
-constexpr int kLdsBytes = kScaleOff + 1024;
-static_assert(store_lds_bytes<kRB, kCB>(kWaves) <= kScaleOff, "store staging must not reach the scales");
+constexpr int kScaleOff = kStages * kStageBytes;             // 2 x 256 per-token scales
+constexpr int kLdsBytes = kScaleOff + 2048;
+static_assert(kWaves * 32 * store_pitch<kCB>() <= kStageBytes, "store staging (2 row blocks) fits one stage");
 
 // Vector-memory operations every step issues per wavefront: 4 for the W
 // tile, 2 for the A fragments, 1 for the position fields (a LoRA step pads
@@ -167,8 +167,14 @@ __device__ __forceinline__ void dma_scale_asm(__amdgpu_buffer_rsrc_t sr, uint32_
   (void)saved;
 }
 
+// Persistent: the grid holds at most one workgroup per CU, and workgroup w
+// computes tiles w, w + G, w + 2G, ... (G = grid size; these run on w's XCD,
+// see tile_coords_of).  All steps of all its tiles form one pipeline: the
+// copies of the next tile's first two steps are in flight while the current
+// tile's epilogue scales and stores it through the one free stage.
+//
 // RING: the LoRA-up runs as extra steps of the LDS ring (r % 8 == 0 and
-// 16-byte W rows).  Otherwise it runs after the k loop from global memory
+// 16-byte W rows).  Otherwise it runs in the epilogue from global memory
 // (odd ranks, K % 8 == 4: shapes outside the fast path).
 template <int KM, bool RING>
 __global__ void __launch_bounds__(kThreads, 1)
@@ -183,19 +189,12 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (N + kTileN - 1) / kTileN;
-  int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int64_t n0 = tn * kTileN;
-  const int64_t mb0 = (tm * kTileM + wm * kWaveM) / 16;   // first 16-token block of this wavefront
+  const int64_t ntiles = tiles_m * tiles_n;
+  const int64_t G = gridDim.x;
+  const int64_t my_tiles = (ntiles - (int64_t)blockIdx.x + G - 1) / G;   // >= 1: grid <= tiles
   const int64_t ksteps = 2 * kpairs;
   const int64_t lsteps = RING && r > 0 ? rsteps : 0;
-  const int64_t total = ksteps + lsteps;
-
-  f32x4 acc[kRB][kCB];
-#pragma unroll
-  for (int i = 0; i < kRB; ++i)
-#pragma unroll
-    for (int j = 0; j < kCB; ++j) acc[i][j] = (f32x4){0, 0, 0, 0};
+  const int64_t spt = ksteps + lsteps;                  // steps per tile
 
   // Every operand of the loop arrives by DMA into a 3-stage LDS ring, two
   // steps ahead; nothing in the loop is a compiler-visible memory load, so
@@ -207,51 +206,82 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, tiles_m * kTileM * 4);
   const __amdgpu_buffer_rsrc_t tr = make_rsrc(tfrag, tiles_m * 16 * rsteps * 2048);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(lora_b, N * r * 2);
-  const uint32_t a_group0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 8192));
-  const uint32_t i_group0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 1024));
   const uint32_t a_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 8192));
   const uint32_t i_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 1024));
-  const uint32_t t_block0 = __builtin_amdgcn_readfirstlane((uint32_t)(tm * 16 * rsteps * 2048));
-  const WTileOffsets wo = w_tile_offsets<kWaves>(K, n0);
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(&lds[0]);
-
-  // Copies of step g (a k-step below ksteps, a LoRA step after) into stage b.
-  auto prefetch = [&](int64_t g, int b) {
-    const uint32_t st = lds_base + (uint32_t)b * kStageBytes;
-    if (RING && g >= ksteps) {
-      dma_lora_tile_asm(tr, br, t_block0, rsteps, g - ksteps, N, r, n0, st);
-      return;
-    }
-    dma_a_tile_asm(ar, ir, a_group0, i_group0, a_gstride, i_gstride, g, st);
-    if constexpr (KM == kAligned8) dma_w_tile_dword<kWaves>(wr, N, K, n0, g * kTileK, &lds[b * kStageBytes]);
-    else dma_w_tile_asm<kWaves>(wr, wo, K, g * kTileK, st, KM == kAligned16);
-  };
   constexpr int kOps = KM == kAligned8 ? 128 / kWaves + 3 : kStepOps;
+
+  // Prefetch cursor: the step the next prefetch copies (tile ordinal, step
+  // within the tile, and that tile's copy offsets).  After the last step of
+  // the last tile it stays there: the extra copies are harmless copies into
+  // free stages.
+  int64_t pc_i = 0, pc_loc = 0, pc_n0 = 0;
+  uint32_t pc_ag0 = 0, pc_ig0 = 0, pc_tb0 = 0;
+  WTileOffsets pc_wo;
+  auto cursor_tile = [&](int64_t i) {
+    int64_t tm, tn;
+    tile_coords_of((int64_t)blockIdx.x + i * G, tiles_m, tiles_n, tm, tn);
+    pc_n0 = tn * kTileN;
+    pc_ag0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 8192));
+    pc_ig0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 1024));
+    pc_tb0 = __builtin_amdgcn_readfirstlane((uint32_t)(tm * 16 * rsteps * 2048));
+    pc_wo = w_tile_offsets<kWaves>(K, pc_n0);
+  };
+  cursor_tile(0);
+  auto prefetch = [&](int b) {
+    const uint32_t st = lds_base + (uint32_t)b * kStageBytes;
+    if (RING && pc_loc >= ksteps) {
+      dma_lora_tile_asm(tr, br, pc_tb0, rsteps, pc_loc - ksteps, N, r, pc_n0, st);
+    } else {
+      dma_a_tile_asm(ar, ir, pc_ag0, pc_ig0, a_gstride, i_gstride, pc_loc, st);
+      if constexpr (KM == kAligned8) dma_w_tile_dword<kWaves>(wr, N, K, pc_n0, pc_loc * kTileK, &lds[b * kStageBytes]);
+      else dma_w_tile_asm<kWaves>(wr, pc_wo, K, pc_loc * kTileK, st, KM == kAligned16);
+    }
+    if (pc_loc + 1 < spt) {
+      ++pc_loc;
+    } else if (pc_i + 1 < my_tiles) {
+      ++pc_i;
+      pc_loc = 0;
+      cursor_tile(pc_i);
+    }
+  };
+  // Per-token scales of tile i into LDS buffer i % 2.
+  auto copy_scales = [&](int64_t i) {
+    int64_t tm, tn;
+    tile_coords_of((int64_t)blockIdx.x + i * G, tiles_m, tiles_n, tm, tn);
+    dma_scale_asm(sr, (uint32_t)(tm * kTileM * 4), lds_base + kScaleOff + (uint32_t)(i & 1) * 1024u);
+  };
 
   const char* b_base0 = &lds[0] + wn * kCB * 2048 + frag_lane_offset(0);
   const char* b_base1 = &lds[0] + wn * kCB * 2048 + frag_lane_offset(1);
   const char* a_base = &lds[0] + kAStageOff + 16 * lane + wm * 8192;
   const char* i_base = &lds[0] + kIStageOff + 16 * lane + wm * 1024;
 
-  // Two barriers per step g (stage b = g % 3):
-  //  * at the top: every wave is done with step g - 1, so its stage
-  //    (b + 2) % 3 is free and the copies of step g + 2 start there (near
-  //    the end, the last step again: a harmless copy into a free stage);
+  // Two barriers per step (stage b):
+  //  * at the top: every wave is done with the previous step, so its stage
+  //    (b + 2) % 3 is free and the copies two steps ahead start there (with
+  //    the next tile's scales on a tile's first step);
   //  * before the last column block: each wave has waited for its copies of
-  //    step g + 1 (only step g + 2's may be in flight), so after the barrier
-  //    stage (b + 1) % 3 is complete.  The last column block's MFMAs then
-  //    overlap the LDS reads of step g + 1's first operands, and the next
-  //    step starts its MFMAs without a load bubble.
-  // A copy issued at the top of step g - 1 thus has until late in step g.
-  auto barrier_top = [&](int64_t g, int b) {
+  //    the next step (only those two steps ahead may be in flight), so after
+  //    the barrier stage (b + 1) % 3 is complete.  The last column block's
+  //    MFMAs then overlap the LDS reads of the next step's first operands,
+  //    and the next step starts its MFMAs without a load bubble.
+  // A copy issued at the top of one step thus has until late in the next.
+  auto barrier_top = [&](int b, int64_t scales_for) {
     __builtin_amdgcn_sched_barrier(0);
     barrier_no_fence();
-    prefetch(g + 2 < total ? g + 2 : total - 1, (b + 2) % kStages);
+    prefetch((b + 2) % kStages);
+    if (scales_for >= 0) copy_scales(scales_for);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto barrier_mid = [&]() {
+  // after_stores: the previous tile's output stores were issued after the
+  // awaited copies and may still be in flight (vmcnt counts them too).
+  constexpr int kStoreOps = store_passes_ops<kRB, kCB, 2>();
+  static_assert(kOps + kStoreOps < 64, "vmcnt field is 6 bits");
+  auto barrier_mid = [&](bool after_stores = false) {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<kOps>();
+    if (after_stores) wait_vm<kOps + kStoreOps>();
+    else wait_vm<kOps>();
     barrier_no_fence();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -269,11 +299,13 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
       af[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_base + b * kStageBytes + rb * 1024));
   };
 
+  f32x4 acc[kRB][kCB];
+
   // One k-step: 32 structured-sparse MFMAs, the W fragments (two 16-byte
   // halves per lane, swizzled tile) read one column block ahead.  The
   // position fields of row blocks 2j and 2j+1 share a 32-bit word (abid).
-  auto kstep = [&](int64_t ks, int b) {
-    barrier_top(ks, b);
+  auto kstep = [&](int b, int64_t scales_for, bool after_stores) {
+    barrier_top(b, scales_for);
     const char* s0 = b_base0 + b * kStageBytes;
     const char* s1 = b_base1 + b * kStageBytes;
     const int bn = b == kStages - 1 ? 0 : b + 1;
@@ -289,7 +321,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
           acc[rb + 1][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb + 1], bf, acc[rb + 1][cb], (int)iw[rb / 2], 0, 1);
         }
       } else {
-        barrier_mid();
+        barrier_mid(after_stores);
         const u32x4 iw_cur = iw;
         iw = *reinterpret_cast<const u32x4*>(i_base + bn * kStageBytes);
         bq0 = *reinterpret_cast<const u32x4*>(b_base0 + bn * kStageBytes);
@@ -317,8 +349,8 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   // One LoRA step: for each half (hi, lo) of alpha T / s, 8 row fragments
   // and 4 B fragments from LDS, 32 dense MFMAs; then the wait and barrier
   // that make the next step's stage complete.
-  auto lstep = [&](int64_t g, int b) {
-    barrier_top(g, b);
+  auto lstep = [&](int b) {
+    barrier_top(b, -1);
     const char* st = &lds[0] + b * kStageBytes + 16 * lane;
     bf16x8 bfr[kCB];
 #pragma unroll
@@ -339,88 +371,119 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     barrier_mid();
   };
 
-  // Prologue: the tile's scales, then steps 0 and 1 (ksteps >= 2 always);
-  // wait for step 0 and read its first operands.
-  dma_scale_asm(sr, (uint32_t)(tm * kTileM * 4), lds_base + kScaleOff);
-  prefetch(0, 0);
-  prefetch(1, 1);
+  // Prologue: the first tile's scales, then its steps 0 and 1 (ksteps >= 2
+  // always); wait for step 0 and read its first operands.
+  copy_scales(0);
+  prefetch(0);
+  prefetch(1);
   barrier_mid();
   load_first(0);
-  // One step per iteration, the stage a runtime index: unrolled copies of
-  // the step get different accumulator registers from the register
-  // allocator, and the copies between them wait on the matrix pipeline.
-  // (After the last k-step the operands read for "the next step" are
-  // unused.)
-  int b = 0;
-#pragma nounroll
-  for (int64_t ks = 0; ks < ksteps; ++ks) {
-    kstep(ks, b);
-    b = b == kStages - 1 ? 0 : b + 1;
-  }
-  if constexpr (RING) {
-    for (int64_t g = ksteps; g < total; ++g) lstep(g, (int)(g % kStages));
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vm<0>();
-  barrier_no_fence();                     // every wave is done with the ring
 
-  if constexpr (!RING) {
-    // LoRA-up from global memory: (alpha T / s)_hi B^T + (alpha T / s)_lo B^T.
-    for (int64_t rs = 0; r > 0 && rs < rsteps; ++rs) {
-      bf16x8 bfr[kCB];
+  int b = 0;
+  for (int64_t i = 0; i < my_tiles; ++i) {
+    int64_t tm, tn;
+    tile_coords_of((int64_t)blockIdx.x + i * G, tiles_m, tiles_n, tm, tn);
+    const int64_t n0 = tn * kTileN;
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) {
-        const int64_t n = n0 + wn * kWaveN + 16 * cb + (lane & 15);
-        const int64_t j = 32 * rs + 8 * (lane >> 4);
-        u32x4 v = (u32x4){0, 0, 0, 0};
-        if (n < N) {
-          const uint16_t* pb = lora_b + n * r + j;
-          if (r % 8 == 0) {
-            if (j + 8 <= r) v = *reinterpret_cast<const u32x4*>(pb);
-          } else {
-            uint16_t e[8];
+    for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) e[t] = (j + t < r) ? pb[t] : (uint16_t)0;
-            v = (u32x4){e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                        e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)};
-          }
-        }
-        bfr[cb] = __builtin_bit_cast(bf16x8, v);
+      for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = (f32x4){0, 0, 0, 0};
+
+    // One step per iteration, the stage a runtime index: unrolled copies of
+    // the step get different accumulator registers from the register
+    // allocator, and the copies between them wait on the matrix pipeline.
+    // The first step also copies the next tile's scales.
+    kstep(b, i + 1 < my_tiles ? i + 1 : -1, i > 0 && N % 8 == 0);
+    b = b == kStages - 1 ? 0 : b + 1;
+#pragma nounroll
+    for (int64_t ks = 1; ks < ksteps; ++ks) {
+      kstep(b, -1, false);
+      b = b == kStages - 1 ? 0 : b + 1;
+    }
+    if constexpr (RING) {
+      for (int64_t g = 0; g < lsteps; ++g) {
+        lstep(b);
+        b = b == kStages - 1 ? 0 : b + 1;
       }
+    }
+    // Epilogue.  Every wave has consumed the last step's stage (the barrier
+    // below), the next stage is complete and the one after is in flight.
+    const int b_last = b == 0 ? kStages - 1 : b - 1;
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_no_fence();
+
+    if constexpr (!RING) {
+      // LoRA-up from global memory: (alpha T / s)_hi B^T + (alpha T / s)_lo B^T.
+      const int64_t mb0 = (tm * kTileM + wm * kWaveM) / 16;
+      for (int64_t rs = 0; r > 0 && rs < rsteps; ++rs) {
+        bf16x8 bfr[kCB];
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        const int64_t mb = mb0 + rb;
+        for (int cb = 0; cb < kCB; ++cb) {
+          const int64_t n = n0 + wn * kWaveN + 16 * cb + (lane & 15);
+          const int64_t j = 32 * rs + 8 * (lane >> 4);
+          u32x4 v = (u32x4){0, 0, 0, 0};
+          if (n < N) {
+            const uint16_t* pb = lora_b + n * r + j;
+            if (r % 8 == 0) {
+              if (j + 8 <= r) v = *reinterpret_cast<const u32x4*>(pb);
+            } else {
+              uint16_t e[8];
 #pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-          const bf16x8 ta = __builtin_bit_cast(bf16x8, tfrag[((mb * rsteps + rs) * 2 + hl) * 64 + lane]);
+              for (int t = 0; t < 8; ++t) e[t] = (j + t < r) ? pb[t] : (uint16_t)0;
+              v = (u32x4){e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
+                          e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)};
+            }
+          }
+          bfr[cb] = __builtin_bit_cast(bf16x8, v);
+        }
 #pragma unroll
-          for (int cb = 0; cb < kCB; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta, bfr[cb], acc[rb][cb], 0, 0, 0);
+        for (int rb = 0; rb < kRB; ++rb) {
+          const int64_t mb = mb0 + rb;
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl) {
+            const bf16x8 ta = __builtin_bit_cast(bf16x8, tfrag[((mb * rsteps + rs) * 2 + hl) * 64 + lane]);
+#pragma unroll
+            for (int cb = 0; cb < kCB; ++cb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta, bfr[cb], acc[rb][cb], 0, 0, 0);
+          }
         }
       }
     }
-  }
 
-  // Per-token compensation scale on the fp32 accumulators.
+    // Per-token compensation scale on the fp32 accumulators.  (Tile i's
+    // scales were copied two tiles' worth of steps ago, or in the prologue.)
+    const char* sbuf = &lds[kScaleOff] + (i & 1) * 1024;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(&lds[kScaleOff] + (wm * kWaveM + 16 * rb + 4 * (lane >> 4)) * 4);
+    for (int rb = 0; rb < kRB; ++rb) {
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(sbuf + (wm * kWaveM + 16 * rb + 4 * (lane >> 4)) * 4);
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
+      for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[rb][cb][i] *= sv[i];
-  }
+        for (int i4 = 0; i4 < 4; ++i4) acc[rb][cb][i4] *= sv[i4];
+    }
 
-  const int64_t m0 = tm * kTileM + wm * kWaveM;
-  if (N % 8 == 0) store_tile_via_lds<kRB, kCB>(acc, lds, y, M, N, m0, n0 + wn * kWaveN);
-  else store_acc_bf16<kRB, kCB>(acc, y, M, N, m0, n0 + wn * kWaveN);
+    const int64_t m0 = tm * kTileM + wm * kWaveM;
+    if (N % 8 == 0) {
+      char* region = &lds[0] + b_last * kStageBytes + wave * (32 * store_pitch<kCB>());
+      store_tile_via_lds_passes<kRB, kCB, 2>(acc, region, y, M, N, m0, n0 + wn * kWaveN);
+    } else {
+      store_acc_bf16<kRB, kCB>(acc, y, M, N, m0, n0 + wn * kWaveN);
+    }
+    // The next tile starts from stage b, complete since the last step's
+    // second barrier.
+    if (i + 1 < my_tiles) load_first(b);
+  }
+  // Drain the remaining (redundant) copies before the workgroup's LDS is
+  // released.
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<0>();
 }
 
 }  // namespace
 
 hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const uint16_t* lora_b,
                               int64_t M, int64_t N, int64_t K, int64_t r, uint16_t* y,
-                              hipStream_t stream) {
+                              int compute_units, hipStream_t stream) {
   const WsLayout L = ws_layout(M, K, r);
   const char* ws = static_cast<const char*>(workspace);
   const u32x4* xv = reinterpret_cast<const u32x4*>(ws + L.off_xv);
@@ -428,7 +491,9 @@ hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const ui
   const float* s = reinterpret_cast<const float*>(ws + L.off_s);
   const u32x4* t = reinterpret_cast<const u32x4*>(ws + L.off_t);
   const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
-  const dim3 grid((unsigned)tiles), block(kThreads);
+  // One persistent workgroup per CU (the LDS allows one), at most one per tile.
+  const int64_t cus = compute_units > 0 ? compute_units : 1;
+  const dim3 grid((unsigned)(tiles < cus ? tiles : cus)), block(kThreads);
   const int64_t kpairs = L.kp / 128, rsteps = L.rp / 32;
   // The k loop runs over the padded K (a multiple of 128): full-K mode
   // needs K itself to be one.
