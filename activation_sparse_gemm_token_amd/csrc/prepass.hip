@@ -257,6 +257,279 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pre-pass with DMA-streamed operands (K % 8 == 0, 0 < r <= 64): one
+// workgroup of 4 wavefronts per 16-token block, wavefront w covering a
+// quarter of the k-steps.  Each wavefront streams its own operands into its
+// own LDS rings with buffer_load_dwordx4 ... lds (whole 128-byte lines, no
+// registers):
+//   * X: 16 tokens x 64 channels (2 KiB) per k-step, 8 stages, 7 steps ahead
+//     (HBM latency);
+//   * A: 16 NCB ranks x 64 channels (2 NCB KiB) per k-step, 3 stages, 2
+//     steps ahead (L2-resident: every workgroup reads all of A).
+// Both tiles use the swizzled row-major layout of the GEMM's W tile
+// (16-byte chunk c of row n in slot c ^ (n & 7)), so the copies read whole
+// lines and the fragment reads are conflict-free.  Only the issuing
+// wavefront reads its rings, so its own vmcnt wait suffices (no barrier).
+// The loads are inline asm, invisible to the compiler; the explicit waits
+// count them exactly, together with the stores of xv and xi (the loop's only
+// other vector-memory operations).
+constexpr int kDWaves = 4;
+constexpr int kXStages = 8, kXAhead = 7;
+constexpr int kAStages = 3, kAAhead = 2;
+
+// NI 1-KiB copies (8 rows x 128 bytes each): instruction i writes LDS
+// lds_addr + 1024 i (through M0) from per-lane source offsets v[i].  No
+// output registers, M0 saved and restored, no SCC write (as the GEMM's copy
+// blocks).
+template <int NI>
+__device__ __forceinline__ void dma_rows_asm(__amdgpu_buffer_rsrc_t rs, const uint32_t (&v)[NI],
+                                             uint32_t lds_addr) {
+  uint32_t saved;
+  if constexpr (NI == 2) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[l0]\n\t"
+        "buffer_load_dwordx4 %[v0], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l1]\n\t"
+        "buffer_load_dwordx4 %[v1], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [v0] "v"(v[0]), [v1] "v"(v[1]), [rs] "s"(rs), [l0] "s"(lds_addr), [l1] "s"(lds_addr + 0x400u)
+        : "memory");
+  } else if constexpr (NI == 4) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[l0]\n\t"
+        "buffer_load_dwordx4 %[v0], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l1]\n\t"
+        "buffer_load_dwordx4 %[v1], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l2]\n\t"
+        "buffer_load_dwordx4 %[v2], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l3]\n\t"
+        "buffer_load_dwordx4 %[v3], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [rs] "s"(rs), [l0] "s"(lds_addr),
+          [l1] "s"(lds_addr + 0x400u), [l2] "s"(lds_addr + 0x800u), [l3] "s"(lds_addr + 0xc00u)
+        : "memory");
+  } else {
+    static_assert(NI == 8, "2, 4 or 8 row blocks");
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[l0]\n\t"
+        "buffer_load_dwordx4 %[v0], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l1]\n\t"
+        "buffer_load_dwordx4 %[v1], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l2]\n\t"
+        "buffer_load_dwordx4 %[v2], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l3]\n\t"
+        "buffer_load_dwordx4 %[v3], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l4]\n\t"
+        "buffer_load_dwordx4 %[v4], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l5]\n\t"
+        "buffer_load_dwordx4 %[v5], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l6]\n\t"
+        "buffer_load_dwordx4 %[v6], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[l7]\n\t"
+        "buffer_load_dwordx4 %[v7], %[rs], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [v4] "v"(v[4]), [v5] "v"(v[5]),
+          [v6] "v"(v[6]), [v7] "v"(v[7]), [rs] "s"(rs), [l0] "s"(lds_addr), [l1] "s"(lds_addr + 0x400u),
+          [l2] "s"(lds_addr + 0x800u), [l3] "s"(lds_addr + 0xc00u), [l4] "s"(lds_addr + 0x1000u),
+          [l5] "s"(lds_addr + 0x1400u), [l6] "s"(lds_addr + 0x1800u), [l7] "s"(lds_addr + 0x1c00u)
+        : "memory");
+  }
+  (void)saved;
+}
+
+// Per-lane source offsets of NI 8-row blocks of a row-major [rows, K] bf16
+// matrix at channel k0 (rows row0 + 8 i + l / 8, source chunk
+// (l % 8) ^ (l / 8)); rows past `rows` and chunks past K point out of range.
+template <int NI>
+__device__ __forceinline__ void rows_offsets(int64_t row0, int64_t rows, int64_t K, int64_t k0,
+                                             uint32_t (&v)[NI]) {
+  const int lane = threadIdx.x & 63;
+  const int64_t k = k0 + 8 * ((lane & 7) ^ (lane >> 3));
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int64_t rw = row0 + 8 * i + (lane >> 3);
+    v[i] = (rw < rows && k + 8 <= K) ? (uint32_t)((rw * K + k) * 2) : kOobOffset;
+  }
+}
+
+// Byte offset, inside a swizzled tile (128-byte rows), of chunk c of row n.
+__device__ __forceinline__ uint32_t swz(int n, int c) { return (uint32_t)(n * 128 + ((c ^ (n & 7)) << 4)); }
+
+template <int NCB>
+__global__ void __launch_bounds__(64 * kDWaves, 1)
+prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora_a,
+                   int64_t M, int64_t K, int64_t r, float alpha,
+                   u32x4* __restrict__ xv, uint16_t* __restrict__ xi, float* __restrict__ s_out,
+                   u32x4* __restrict__ t_out, int64_t ksteps, int64_t rsteps) {
+  static_assert(NCB == 2 || NCB == 4, "ranks 32 or 64");
+  constexpr int kXBytes = 2048;                       // 16 tokens x 128 B
+  constexpr int kABytes = NCB * 2048;                 // 16 NCB ranks x 128 B
+  constexpr int kWaveBytes = kXStages * kXBytes + kAStages * kABytes;
+  constexpr int kXOps = 2, kAOps = 2 * NCB;
+  // Reduction arrays, aliased onto the rings after the loop.
+  struct Red {
+    float l[kDWaves][2][16];
+    float s[16];
+    float t[kDWaves][16][NCB * 16 + 1];
+  };
+  static_assert((int)sizeof(Red) <= kDWaves * kWaveBytes, "reduction fits in the rings");
+  __shared__ __attribute__((aligned(16))) char lds[kDWaves * kWaveBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Same XCD-grouped block mapping as prepass_kernel.
+  const int64_t ngroups = 2 * ((M + 255) / 256);
+  const int64_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  const int64_t grp_id = 8 * (local / 8) + xcd;
+  if (grp_id >= ngroups) return;
+  const int64_t mb = 8 * grp_id + local % 8;
+  const int64_t grp = mb >> 3, sub = mb & 7;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, M * K * 2);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(lora_a, r * K * 2);
+  const int64_t ks_begin = wave * ksteps / kDWaves, ks_end = (wave + 1) * ksteps / kDWaves;
+  const int64_t nks = ks_end - ks_begin;             // uniform per wavefront
+  char* const ring = lds + wave * kWaveBytes;
+  const uint32_t ring_addr = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(ring));
+
+  // Copies issued together: A of step t_a (if t_a >= 0) first, then X of
+  // step t_x, each clamped to the wavefront's last step (a harmless repeat
+  // into a stage nobody reads again).  A goes first so that waiting for
+  // A(t) -- with in-order completion -- does not also wait for the X copy
+  // issued far ahead alongside it.
+  auto copy_step = [&](int64_t t_x, int64_t t_a) {
+    if (t_a >= 0) {
+      const int64_t tc = t_a < nks ? t_a : nks - 1;
+      uint32_t v[kAOps];
+      rows_offsets<kAOps>(0, r, K, (ks_begin + tc) * 64, v);
+      dma_rows_asm<kAOps>(ar, v, ring_addr + kXStages * kXBytes + (uint32_t)(t_a % kAStages) * kABytes);
+    }
+    const int64_t tc = t_x < nks ? t_x : nks - 1;
+    uint32_t v[kXOps];
+    rows_offsets<kXOps>(mb * 16, M, K, (ks_begin + tc) * 64, v);
+    dma_rows_asm<kXOps>(xr, v, ring_addr + (uint32_t)(t_x % kXStages) * kXBytes);
+  };
+
+  float lk = 0.f, lp = 0.f;
+  f32x4 tk[NCB], tp[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) { tk[c] = (f32x4){0, 0, 0, 0}; tp[c] = (f32x4){0, 0, 0, 0}; }
+
+  // Lane l: token l % 16, channels 16 (l / 16) + [0, 16) = chunks 2q, 2q + 1;
+  // B operand halves of rank row l % 16: chunks l / 16 and 4 + l / 16.
+  const int tok = lane & 15, q = lane >> 4;
+  const uint32_t xo0 = swz(tok, 2 * q), xo1 = swz(tok, 2 * q + 1);
+  const uint32_t bo0 = swz(tok, q), bo1 = swz(tok, 4 + q);
+
+  if (nks > 0) {
+    // Prologue in the steady-state issue order: step t issues A(t + 2), then
+    // X(t + 7); X(0..4) first, then (A(0), X(5)), (A(1), X(6)).
+    for (int i = 0; i < kXAhead - kAAhead; ++i) copy_step(i, -1);
+    for (int i = 0; i < kAAhead; ++i) copy_step(kXAhead - kAAhead + i, i);
+    for (int64_t t = 0; t < nks; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      copy_step(t + kXAhead, t + kAAhead);
+      // Wait for step t's copies (X(t) was issued before A(t)).  Younger
+      // than A(t): the X copy issued with it, the copies of the two steps
+      // after it (the second just issued) and the 2 stores (xv, xi) of each
+      // step since -- fewer in the first steps.  Vector-memory operations
+      // complete in issue order, so the count is exact.
+      constexpr int kC = kXOps + 2 * (kAOps + kXOps);
+      if (t >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kC + 4) : "memory");
+      else if (t == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kC + 2) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kC) : "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const char* xs = ring + (t % kXStages) * kXBytes;
+      const u32x4 c0 = *reinterpret_cast<const u32x4*>(xs + xo0);
+      const u32x4 c1 = *reinterpret_cast<const u32x4*>(xs + xo1);
+      const uint32_t w[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+      Quad qd;
+      select_quad(w, qd, lk, lp);
+      const int64_t kst = ks_begin + t;
+      xv[((grp * ksteps + kst) * 8 + sub) * 64 + lane] = qd.kept;
+      xi[((grp * ksteps + kst) * 64 + lane) * 8 + sub] = (uint16_t)qd.kcode;
+      const char* as = ring + kXStages * kXBytes + (t % kAStages) * kABytes;
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(as + c * 2048 + bo0);
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(as + c * 2048 + bo1);
+        const bf16x16 bf = __builtin_bit_cast(bf16x16, (u32x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
+        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, qd.kept), bf, tk[c], (int)qd.kcode, 0, 0);
+        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, qd.pruned), bf, tp[c], (int)qd.pcode, 0, 0);
+      }
+    }
+  }
+  // Drain the repeated copies before the rings become reduction arrays.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  Red& red = *reinterpret_cast<Red*>(lds);
+  // Per-token L1 sums: lanes l, l^16, l^32, l^48 share a token; then across
+  // wavefronts in a fixed order.
+  lk += __shfl_xor(lk, 16, 64);
+  lk += __shfl_xor(lk, 32, 64);
+  lp += __shfl_xor(lp, 16, 64);
+  lp += __shfl_xor(lp, 32, 64);
+  if (lane < 16) { red.l[wave][0][lane] = lk; red.l[wave][1][lane] = lp; }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kDWaves; ++w2) { a += red.l[w2][0][threadIdx.x]; b += red.l[w2][1][threadIdx.x]; }
+    const float sc = a > 0.f ? (a + b) / a : 1.0f;
+    red.s[threadIdx.x] = sc;
+    s_out[mb * 16 + threadIdx.x] = sc;
+  }
+  __syncthreads();
+  // Accumulator layout of a 16x16 block: lane l holds column l % 16 of rows
+  // 4 (l / 16) + i.  T_w = T_pruned + (1 - s) T_kept per wavefront, then
+  // summed over wavefronts in a fixed order.
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 4 * (lane >> 4) + i;
+      red.t[wave][rr][c * 16 + (lane & 15)] = tp[c][i] + (1.0f - red.s[rr]) * tk[c][i];
+    }
+  }
+  __syncthreads();
+  // Output fragment (rs, l): token l % 16, rank columns 32 rs + 8 (l / 16) + [0, 8).
+  const int64_t frag = threadIdx.x;
+  if (frag < rsteps * 64) {
+    const int rs = (int)(frag >> 6), fl = (int)(frag & 63);
+    const int rr = fl & 15;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      float v[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int col = 32 * rs + 8 * (fl >> 4) + j + e;
+        float a = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kDWaves; ++w2) a += red.t[w2][rr][col];
+        v[e] = alpha * a / red.s[rr];
+      }
+      const uint32_t h = pack_bf16x2(v[0], v[1]);
+      hi[j / 2] = h;
+      lo[j / 2] = pack_bf16x2(v[0] - bf16_lo_to_f32(h), v[1] - bf16_hi_to_f32(h));
+    }
+    t_out[((mb * rsteps + rs) * 2 + 0) * 64 + fl] = (u32x4){hi[0], hi[1], hi[2], hi[3]};
+    t_out[((mb * rsteps + rs) * 2 + 1) * 64 + fl] = (u32x4){lo[0], lo[1], lo[2], lo[3]};
+  }
+}
+
 template <bool A16>
 hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M, int64_t K,
                             int64_t r, float alpha, const WsLayout& L, char* ws, hipStream_t stream) {
@@ -270,6 +543,20 @@ hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M
   u32x4* t = reinterpret_cast<u32x4*>(ws + L.off_t);
   const int64_t kpairs = L.kp / 128, rsteps = L.rp / 32;
   const int ncb = (int)(L.rp / 16);
+  if constexpr (A16) {
+    // r <= 64: the DMA-streamed pre-pass, one workgroup of 4 wavefronts per
+    // 16-token block (same grid and mapping).
+    const dim3 dblock(64 * kDWaves);
+    const int64_t ksteps = L.kp / 64;
+    if (r > 0 && ncb <= 2) {
+      prepass_dma_kernel<2><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
+      return hipGetLastError();
+    }
+    if (r > 0 && ncb <= 4) {
+      prepass_dma_kernel<4><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
+      return hipGetLastError();
+    }
+  }
   if (r == 0)
     prepass_kernel<A16, 0><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, 0);
   else if (ncb <= 2)
