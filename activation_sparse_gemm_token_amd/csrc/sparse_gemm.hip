@@ -51,43 +51,82 @@ static_assert(kWaves * 32 * store_pitch<kCB>() <= kStageBytes, "store staging (2
 constexpr int kWOps = 32 / kWaves;
 constexpr int kStepOps = kWOps + 3;
 
-// Copies the compressed A operand of one k-step into an LDS stage: thread
-// (wave v, i < 2) moves fragment c = 2 v + i (16-token block c % 8 of group
-// c / 8) with one buffer_load_dwordx4 ... lds, and 256 bytes of the position
-// fields (part v % 4 of group v / 4's 1 KiB) with one buffer_load_dword ...
-// lds.  Same rules as dma_w_tile_asm: no output registers, M0 saved and
-// restored, no SCC write.  The instruction offset of a buffer ... lds load
-// is added to the LDS address too, so every offset is carried by the scalar
-// offset operand.  3 vector-memory operations.
-__device__ __forceinline__ void dma_a_tile_asm(__amdgpu_buffer_rsrc_t ar, __amdgpu_buffer_rsrc_t ir,
-                                               uint32_t a_group0, uint32_t i_group0, uint32_t a_gstride,
-                                               uint32_t i_gstride, int64_t ks, uint32_t lds_stage_addr) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t g = wave >> 2;                       // fragments 2v, 2v+1 lie in group v / 4
-  const uint32_t a_so = __builtin_amdgcn_readfirstlane(a_group0 + g * a_gstride + (uint32_t)ks * 8192u +
-                                                       (wave & 3u) * 2048u);
-  const uint32_t la = __builtin_amdgcn_readfirstlane(lds_stage_addr + kAStageOff + wave * 2048u);
-  const uint32_t i_so = __builtin_amdgcn_readfirstlane(i_group0 + g * i_gstride + (uint32_t)ks * 1024u +
-                                                       (wave & 3u) * 256u);
-  const uint32_t li = __builtin_amdgcn_readfirstlane(lds_stage_addr + kIStageOff + wave * 256u);
-  const uint32_t va = 16u * lane, vi = 4u * lane;
+// Copies of one k-step, issued by every wavefront into the stage at LDS
+// address `stage`, 7 vector-memory operations:
+//  * its 32 rows of the W tile: 4 buffer_load_dwordx4 ... lds of 8 rows x
+//    128 bytes (whole lines, swizzled as described for the W tile);
+//    per-lane row offsets w_v, w1, w2, w3 (VGPR), channel offset w_so (SGPR);
+//  * A fragments 2 v and 2 v + 1 (16-token block 2 v % 8 + [0, 2) of group
+//    v / 4): one 1 KiB buffer_load_dwordx4 ... lds each, source a_so; the
+//    second uses the instruction offset 1024, which moves the global and
+//    the LDS address alike;
+//  * 256 bytes of the position fields (part v % 4 of group v / 4) with one
+//    buffer_load_dword ... lds, source i_so.
+// The block builds every LDS destination in M0 from `stage` and the
+// wavefront's constant offsets (lw, la, li), saves and restores M0, and
+// keeps one wait state between each M0 write and the copy that reads it.
+// It clobbers SCC.  s_nop 4 covers a VALU write of an SGPR operand right
+// before the block.  Nothing here is visible to the compiler as a load: the
+// caller waits with explicit vmcnt counts.
+__device__ __forceinline__ void dma_kstep_asm(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t ar,
+                                              __amdgpu_buffer_rsrc_t ir, uint32_t w_v, uint32_t w1,
+                                              uint32_t w2, uint32_t w3, uint32_t w_so, uint32_t a_so,
+                                              uint32_t i_so, uint32_t va, uint32_t vi, uint32_t stage,
+                                              uint32_t lw, uint32_t la, uint32_t li) {
   uint32_t saved;
   asm volatile(
       "s_nop 4\n\t"
       "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[la0]\n\t"
-      "buffer_load_dwordx4 %[va], %[ar], %[aso0] offen lds\n\t"
-      "s_mov_b32 m0, %[la1]\n\t"
-      "buffer_load_dwordx4 %[va], %[ar], %[aso1] offen lds\n\t"
-      "s_mov_b32 m0, %[li0]\n\t"
-      "buffer_load_dword %[vi], %[ir], %[iso0] offen lds\n\t"
+      "s_add_u32 m0, %[st], %[lw]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[w0], %[wr], %[wso] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[w1], %[wr], %[wso] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[w2], %[wr], %[wso] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[w3], %[wr], %[wso] offen lds\n\t"
+      "s_add_u32 m0, %[st], %[la]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[va], %[ar], %[aso] offen lds\n\t"
+      "buffer_load_dwordx4 %[va], %[ar], %[aso] offen offset:1024 lds\n\t"
+      "s_add_u32 m0, %[st], %[li]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %[vi], %[ir], %[iso] offen lds\n\t"
       "s_mov_b32 m0, %[sv]"
       : [sv] "=&s"(saved)
-      : [va] "v"(va), [vi] "v"(vi), [ar] "s"(ar), [ir] "s"(ir),
-        [aso0] "s"(a_so), [aso1] "s"(a_so + 1024u), [iso0] "s"(i_so),
-        [la0] "s"(la), [la1] "s"(la + 1024u), [li0] "s"(li)
-      : "memory");
+      : [w0] "v"(w_v), [w1] "v"(w1), [w2] "v"(w2), [w3] "v"(w3), [va] "v"(va), [vi] "v"(vi),
+        [wr] "s"(wr), [ar] "s"(ar), [ir] "s"(ir), [wso] "s"(w_so), [aso] "s"(a_so), [iso] "s"(i_so),
+        [st] "s"(stage), [lw] "s"(lw), [la] "s"(la), [li] "s"(li)
+      : "memory", "scc");
+  (void)saved;
+}
+
+// The A fragments and position fields of dma_kstep_asm alone (3
+// operations), for rows of W that are only 8-byte aligned (K % 8 == 4),
+// whose tile goes through the compiler-visible dword copy.
+__device__ __forceinline__ void dma_a_tile_asm(__amdgpu_buffer_rsrc_t ar, __amdgpu_buffer_rsrc_t ir,
+                                               uint32_t a_so, uint32_t i_so, uint32_t va, uint32_t vi,
+                                               uint32_t stage, uint32_t la, uint32_t li) {
+  uint32_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_add_u32 m0, %[st], %[la]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[va], %[ar], %[aso] offen lds\n\t"
+      "buffer_load_dwordx4 %[va], %[ar], %[aso] offen offset:1024 lds\n\t"
+      "s_add_u32 m0, %[st], %[li]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %[vi], %[ir], %[iso] offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [va] "v"(va), [vi] "v"(vi), [ar] "s"(ar), [ir] "s"(ir), [aso] "s"(a_so), [iso] "s"(i_so),
+        [st] "s"(stage), [la] "s"(la), [li] "s"(li)
+      : "memory", "scc");
   (void)saved;
 }
 
@@ -120,18 +159,25 @@ __device__ __forceinline__ void dma_lora_tile_asm(__amdgpu_buffer_rsrc_t tr, __a
       "s_nop 4\n\t"
       "s_mov_b32 %[sv], m0\n\t"
       "s_mov_b32 m0, %[lt0]\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %[vt], %[tr], %[ts0] offen lds\n\t"
       "s_mov_b32 m0, %[lt1]\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %[vt], %[tr], %[ts1] offen lds\n\t"
       "s_mov_b32 m0, %[lt2]\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %[vt], %[tr], %[ts2] offen lds\n\t"
       "s_mov_b32 m0, %[lt3]\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %[vt], %[tr], %[ts3] offen lds\n\t"
       "s_mov_b32 m0, %[lb0]\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %[vb0], %[br], 0 offen lds\n\t"
       "s_mov_b32 m0, %[lb1]\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %[vb1], %[br], 0 offen lds\n\t"
       "s_mov_b32 m0, %[lb1]\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %[vb1], %[br], 0 offen lds\n\t"
       "s_mov_b32 m0, %[sv]"
       : [sv] "=&s"(saved)
@@ -147,18 +193,17 @@ __device__ __forceinline__ void dma_lora_tile_asm(__amdgpu_buffer_rsrc_t tr, __a
 // 64 each with one dword DMA.  (The other wavefronts issue nothing; the
 // vmcnt waits after it only bound later operations, so they hold for both.)
 __device__ __forceinline__ void dma_scale_asm(__amdgpu_buffer_rsrc_t sr, uint32_t row0_bytes,
-                                              uint32_t lds_scale_addr) {
-  const int lane = threadIdx.x & 63;
+                                              uint32_t lds_scale_addr, uint32_t v /* 4 lane */) {
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave >= 4) return;
   const uint32_t so = __builtin_amdgcn_readfirstlane(row0_bytes + 256u * wave);
   const uint32_t ls = __builtin_amdgcn_readfirstlane(lds_scale_addr + 256u * wave);
-  const uint32_t v = 4u * lane;
   uint32_t saved;
   asm volatile(
       "s_nop 4\n\t"
       "s_mov_b32 %[sv], m0\n\t"
       "s_mov_b32 m0, %[ls]\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dword %[v], %[sr], %[so] offen lds\n\t"
       "s_mov_b32 m0, %[sv]"
       : [sv] "=&s"(saved)
@@ -190,11 +235,11 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (N + kTileN - 1) / kTileN;
   const int64_t ntiles = tiles_m * tiles_n;
-  const int64_t G = gridDim.x;
-  const int64_t my_tiles = (ntiles - (int64_t)blockIdx.x + G - 1) / G;   // >= 1: grid <= tiles
-  const int64_t ksteps = 2 * kpairs;
-  const int64_t lsteps = RING && r > 0 ? rsteps : 0;
-  const int64_t spt = ksteps + lsteps;                  // steps per tile
+  const int G = gridDim.x;
+  const int my_tiles = (int)((ntiles - (int64_t)blockIdx.x + G - 1) / G);   // >= 1: grid <= tiles
+  const int ksteps = 2 * (int)kpairs;
+  const int lsteps = RING && r > 0 ? (int)rsteps : 0;
+  const int spt = ksteps + lsteps;                      // steps per tile
 
   // Every operand of the loop arrives by DMA into a 3-stage LDS ring, two
   // steps ahead; nothing in the loop is a compiler-visible memory load, so
@@ -206,39 +251,65 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(s, tiles_m * kTileM * 4);
   const __amdgpu_buffer_rsrc_t tr = make_rsrc(tfrag, tiles_m * 16 * rsteps * 2048);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(lora_b, N * r * 2);
+  // Byte offsets below are 32-bit: the host keeps every tensor and
+  // workspace region (with 256 rows of padding) under 2 GiB.
   const uint32_t a_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 8192));
   const uint32_t i_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 1024));
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(&lds[0]);
   constexpr int kOps = KM == kAligned8 ? 128 / kWaves + 3 : kStepOps;
 
-  // Prefetch cursor: the step the next prefetch copies (tile ordinal, step
-  // within the tile, and that tile's copy offsets).  After the last step of
-  // the last tile it stays there: the extra copies are harmless copies into
-  // free stages.
-  int64_t pc_i = 0, pc_loc = 0, pc_n0 = 0;
-  uint32_t pc_ag0 = 0, pc_ig0 = 0, pc_tb0 = 0;
-  WTileOffsets pc_wo;
-  auto cursor_tile = [&](int64_t i) {
+  // The wavefront's share of a k-step copy: LDS offsets inside a stage and
+  // per-lane source offsets (see dma_kstep_asm).
+  const uint32_t lw = __builtin_amdgcn_readfirstlane(128u * 32u * (uint32_t)wave);
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)kAStageOff + 2048u * (uint32_t)wave);
+  const uint32_t li = __builtin_amdgcn_readfirstlane((uint32_t)kIStageOff + 256u * (uint32_t)wave);
+  const uint32_t row8 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * K));
+  const uint32_t k_lane = 8u * (uint32_t)((lane & 7) ^ (lane >> 3));
+  const uint32_t va = 16u * (uint32_t)lane, vi = 4u * (uint32_t)lane;
+  const uint32_t a_wave = __builtin_amdgcn_readfirstlane((uint32_t)(wave >> 2) * a_gstride + (uint32_t)(wave & 3) * 2048u);
+  const uint32_t i_wave = __builtin_amdgcn_readfirstlane((uint32_t)(wave >> 2) * i_gstride + (uint32_t)(wave & 3) * 256u);
+
+  // Prefetch cursor: the step the next prefetch copies (tile ordinal and
+  // step within the tile) and, for its k-steps, the copy offsets, advanced
+  // by a constant per step.  After the last step of the last tile it stays
+  // there: the extra copies are harmless repeats into free stages.
+  int pc_i = 0, pc_loc = 0;
+  int64_t pc_n0 = 0;
+  uint32_t pc_tb0 = 0, pc_wso = 0, pc_aso = 0, pc_iso = 0, pc_wv = 0;
+  auto cursor_tile = [&](int i) {
     int64_t tm, tn;
-    tile_coords_of((int64_t)blockIdx.x + i * G, tiles_m, tiles_n, tm, tn);
+    tile_coords_of((int64_t)blockIdx.x + (int64_t)i * G, tiles_m, tiles_n, tm, tn);
     pc_n0 = tn * kTileN;
-    pc_ag0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 8192));
-    pc_ig0 = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 1024));
+    pc_aso = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 8192) + a_wave);
+    pc_iso = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 1024) + i_wave);
     pc_tb0 = __builtin_amdgcn_readfirstlane((uint32_t)(tm * 16 * rsteps * 2048));
-    pc_wo = w_tile_offsets<kWaves>(K, pc_n0);
+    pc_wso = 0;
+    pc_wv = (uint32_t)(((pc_n0 + 32 * wave + (lane >> 3)) * K) * 2) + 2u * k_lane;
   };
   cursor_tile(0);
-  auto prefetch = [&](int b) {
-    const uint32_t st = lds_base + (uint32_t)b * kStageBytes;
-    if (RING && pc_loc >= ksteps) {
-      dma_lora_tile_asm(tr, br, pc_tb0, rsteps, pc_loc - ksteps, N, r, pc_n0, st);
+  auto prefetch = [&](uint32_t st_off) {
+    const uint32_t st = lds_base + st_off;
+    const bool kcopy = !RING || pc_loc < ksteps;
+    if (kcopy) {
+      if constexpr (KM == kAligned8) {
+        dma_a_tile_asm(ar, ir, pc_aso, pc_iso, va, vi, st, la, li);
+        dma_w_tile_dword<kWaves>(wr, N, K, pc_n0, (int64_t)pc_loc * kTileK, &lds[st_off]);
+      } else {
+        uint32_t w0 = pc_wv, w1 = pc_wv + row8, w2 = pc_wv + 2 * row8, w3 = pc_wv + 3 * row8;
+        // Channel tail (kAligned16): chunks past K point out of the buffer
+        // (the range check covers the VGPR and the scalar offset together).
+        if (KM == kAligned16 && (int64_t)pc_loc * kTileK + k_lane + 8 > K)
+          w0 = w1 = w2 = w3 = kOobOffset - pc_wso;
+        dma_kstep_asm(wr, ar, ir, w0, w1, w2, w3, pc_wso, pc_aso, pc_iso, va, vi, st, lw, la, li);
+      }
     } else {
-      dma_a_tile_asm(ar, ir, pc_ag0, pc_ig0, a_gstride, i_gstride, pc_loc, st);
-      if constexpr (KM == kAligned8) dma_w_tile_dword<kWaves>(wr, N, K, pc_n0, pc_loc * kTileK, &lds[b * kStageBytes]);
-      else dma_w_tile_asm<kWaves>(wr, pc_wo, K, pc_loc * kTileK, st, KM == kAligned16);
+      dma_lora_tile_asm(tr, br, pc_tb0, rsteps, pc_loc - ksteps, N, r, pc_n0, st);
     }
     if (pc_loc + 1 < spt) {
       ++pc_loc;
+      pc_wso += 2u * kTileK;
+      pc_aso += 8192u;
+      pc_iso += 1024u;
     } else if (pc_i + 1 < my_tiles) {
       ++pc_i;
       pc_loc = 0;
@@ -249,7 +320,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   auto copy_scales = [&](int64_t i) {
     int64_t tm, tn;
     tile_coords_of((int64_t)blockIdx.x + i * G, tiles_m, tiles_n, tm, tn);
-    dma_scale_asm(sr, (uint32_t)(tm * kTileM * 4), lds_base + kScaleOff + (uint32_t)(i & 1) * 1024u);
+    dma_scale_asm(sr, (uint32_t)(tm * kTileM * 4), lds_base + kScaleOff + (uint32_t)(i & 1) * 1024u, vi);
   };
 
   const char* b_base0 = &lds[0] + wn * kCB * 2048 + frag_lane_offset(0);
@@ -257,46 +328,54 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   const char* a_base = &lds[0] + kAStageOff + 16 * lane + wm * 8192;
   const char* i_base = &lds[0] + kIStageOff + 16 * lane + wm * 1024;
 
-  // Two barriers per step (stage b):
-  //  * at the top: every wave is done with the previous step, so its stage
-  //    (b + 2) % 3 is free and the copies two steps ahead start there (with
-  //    the next tile's scales on a tile's first step);
-  //  * before the last column block: each wave has waited for its copies of
-  //    the next step (only those two steps ahead may be in flight), so after
-  //    the barrier stage (b + 1) % 3 is complete.  The last column block's
-  //    MFMAs then overlap the LDS reads of the next step's first operands,
-  //    and the next step starts its MFMAs without a load bubble.
-  // A copy issued at the top of one step thus has until late in the next.
-  auto barrier_top = [&](int b, int64_t scales_for) {
-    __builtin_amdgcn_sched_barrier(0);
-    barrier_no_fence();
-    prefetch((b + 2) % kStages);
-    if (scales_for >= 0) copy_scales(scales_for);
-    __builtin_amdgcn_sched_barrier(0);
+  // Stages by LDS byte offset: o_cur is the step's stage, o_nxt the next
+  // one, o_pf the one after (in flight); the three rotate after each step.
+  uint32_t o_cur = 0, o_nxt = kStageBytes, o_pf = 2 * kStageBytes;
+  auto rotate = [&]() {
+    const uint32_t t = o_cur;
+    o_cur = o_nxt;
+    o_nxt = o_pf;
+    o_pf = t;
   };
+
+  // One barrier per step, once the wave has read all of the step's operands
+  // from LDS (the last column block's W fragments included) and waited for
+  // its own copies of the next step (only those of the step after may still
+  // be in flight).  After it, stage o_nxt is complete for every wave and
+  // stage o_cur is free: it is refilled at once with the step three ahead,
+  // while the step's last MFMAs run.  A copy thus has two steps to land.
   // after_stores: the previous tile's output stores were issued after the
   // awaited copies and may still be in flight (vmcnt counts them too).
   constexpr int kStoreOps = store_passes_ops<kRB, kCB, 2>();
-  static_assert(kOps + kStoreOps < 64, "vmcnt field is 6 bits");
-  auto barrier_mid = [&](bool after_stores = false) {
+  static_assert(2 * kOps + kStoreOps < 64, "vmcnt field is 6 bits");
+  auto step_barrier = [&](bool after_stores) {
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (after_stores) wait_vm<kOps + kStoreOps>();
     else wait_vm<kOps>();
     barrier_no_fence();
     __builtin_amdgcn_sched_barrier(0);
   };
+  // The refill of the stage just consumed, plus the next tile's scales on a
+  // tile's first step.
+  auto refill = [&](int64_t scales_for) {
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch(o_cur);
+    if (scales_for >= 0) copy_scales(scales_for);
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // Operands a k-step starts with: the position fields, the 8 A fragments
-  // and the first column block of W, read from stage b.
+  // and the first column block of W, read from the stage at offset o.
   u32x4 iw, bq0, bq1;
   bf16x8 af[kRB];
-  auto load_first = [&](int b) {
-    iw = *reinterpret_cast<const u32x4*>(i_base + b * kStageBytes);
-    bq0 = *reinterpret_cast<const u32x4*>(b_base0 + b * kStageBytes);
-    bq1 = *reinterpret_cast<const u32x4*>(b_base1 + b * kStageBytes);
+  auto load_first = [&](uint32_t o) {
+    iw = *reinterpret_cast<const u32x4*>(i_base + o);
+    bq0 = *reinterpret_cast<const u32x4*>(b_base0 + o);
+    bq1 = *reinterpret_cast<const u32x4*>(b_base1 + o);
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
-      af[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_base + b * kStageBytes + rb * 1024));
+      af[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_base + o + rb * 1024));
   };
 
   f32x4 acc[kRB][kCB];
@@ -304,11 +383,13 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   // One k-step: 32 structured-sparse MFMAs, the W fragments (two 16-byte
   // halves per lane, swizzled tile) read one column block ahead.  The
   // position fields of row blocks 2j and 2j+1 share a 32-bit word (abid).
-  auto kstep = [&](int b, int64_t scales_for, bool after_stores) {
-    barrier_top(b, scales_for);
-    const char* s0 = b_base0 + b * kStageBytes;
-    const char* s1 = b_base1 + b * kStageBytes;
-    const int bn = b == kStages - 1 ? 0 : b + 1;
+  // The last column block runs after the step's barrier, together with the
+  // reads of the next step's first operands and the refill (deferred to the
+  // epilogue on a tile's last step, whose stage the epilogue uses).
+  auto kstep = [&](int64_t scales_for, bool after_stores, bool defer) {
+    const char* s0 = b_base0 + o_cur;
+    const char* s1 = b_base1 + o_cur;
+    const uint32_t on = o_nxt;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
       const bf16x16 bf = __builtin_bit_cast(bf16x16, (u32x8){bq0[0], bq0[1], bq0[2], bq0[3], bq1[0], bq1[1], bq1[2], bq1[3]});
@@ -321,17 +402,17 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
           acc[rb + 1][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb + 1], bf, acc[rb + 1][cb], (int)iw[rb / 2], 0, 1);
         }
       } else {
-        barrier_mid(after_stores);
+        step_barrier(after_stores);
         const u32x4 iw_cur = iw;
-        iw = *reinterpret_cast<const u32x4*>(i_base + bn * kStageBytes);
-        bq0 = *reinterpret_cast<const u32x4*>(b_base0 + bn * kStageBytes);
-        bq1 = *reinterpret_cast<const u32x4*>(b_base1 + bn * kStageBytes);
+        iw = *reinterpret_cast<const u32x4*>(i_base + on);
+        bq0 = *reinterpret_cast<const u32x4*>(b_base0 + on);
+        bq1 = *reinterpret_cast<const u32x4*>(b_base1 + on);
 #pragma unroll
         for (int rb = 0; rb < kRB; rb += 2) {
           acc[rb][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb], bf, acc[rb][cb], (int)iw_cur[rb / 2], 0, 0);
           acc[rb + 1][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb + 1], bf, acc[rb + 1][cb], (int)iw_cur[rb / 2], 0, 1);
-          af[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_base + bn * kStageBytes + rb * 1024));
-          af[rb + 1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_base + bn * kStageBytes + (rb + 1) * 1024));
+          af[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_base + on + rb * 1024));
+          af[rb + 1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a_base + on + (rb + 1) * 1024));
         }
         // Interleave: the 3 reads above first, then one MFMA and one read
         // (the A fragment the MFMA has just consumed) at a time.
@@ -342,16 +423,18 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (!defer) refill(scales_for);
       }
     }
+    if (defer && scales_for >= 0) copy_scales(scales_for);
+    rotate();
   };
 
   // One LoRA step: for each half (hi, lo) of alpha T / s, 8 row fragments
-  // and 4 B fragments from LDS, 32 dense MFMAs; then the wait and barrier
-  // that make the next step's stage complete.
-  auto lstep = [&](int b) {
-    barrier_top(b, -1);
-    const char* st = &lds[0] + b * kStageBytes + 16 * lane;
+  // and 4 B fragments from LDS, 32 dense MFMAs; the barrier comes once the
+  // lo half is read, the refill behind it.
+  auto lstep = [&](bool defer) {
+    const char* st = &lds[0] + o_cur + 16 * lane;
     bf16x8 bfr[kCB];
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
@@ -362,56 +445,60 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
         ta[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + ((wm * kRB + rb) * 2 + hl) * 1024));
+      if (hl == 1) {
+        step_barrier(false);
+        if (!defer) refill(-1);
+      }
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta[rb], bfr[cb], acc[rb][cb], 0, 0, 0);
     }
-    barrier_mid();
+    rotate();
   };
 
-  // Prologue: the first tile's scales, then its steps 0 and 1 (ksteps >= 2
-  // always); wait for step 0 and read its first operands.
+  // Prologue: the first tile's scales, then the copies of steps 0, 1 and 2;
+  // wait for step 0's and read its first operands.
   copy_scales(0);
   prefetch(0);
-  prefetch(1);
-  barrier_mid();
+  prefetch(kStageBytes);
+  prefetch(2 * kStageBytes);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<2 * kOps>();
+  barrier_no_fence();
+  __builtin_amdgcn_sched_barrier(0);
   load_first(0);
 
-  int b = 0;
-  for (int64_t i = 0; i < my_tiles; ++i) {
+  for (int i = 0; i < my_tiles; ++i) {
     int64_t tm, tn;
-    tile_coords_of((int64_t)blockIdx.x + i * G, tiles_m, tiles_n, tm, tn);
+    tile_coords_of((int64_t)blockIdx.x + (int64_t)i * G, tiles_m, tiles_n, tm, tn);
     const int64_t n0 = tn * kTileN;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = (f32x4){0, 0, 0, 0};
 
-    // One step per iteration, the stage a runtime index: unrolled copies of
-    // the step get different accumulator registers from the register
+    // One step per iteration, the stage a runtime offset: unrolled copies
+    // of the step get different accumulator registers from the register
     // allocator, and the copies between them wait on the matrix pipeline.
-    // The first step also copies the next tile's scales.
-    kstep(b, i + 1 < my_tiles ? i + 1 : -1, i > 0 && N % 8 == 0);
-    b = b == kStages - 1 ? 0 : b + 1;
+    // The first step also copies the next tile's scales; the tile's last
+    // step leaves its refill to the epilogue.
+    const int64_t next_scales = i + 1 < my_tiles ? i + 1 : -1;
+    const bool after_stores = i > 0 && N % 8 == 0;
+    kstep(next_scales, after_stores, lsteps == 0 && ksteps == 1);
 #pragma nounroll
-    for (int64_t ks = 1; ks < ksteps; ++ks) {
-      kstep(b, -1, false);
-      b = b == kStages - 1 ? 0 : b + 1;
-    }
+    for (int ks = 1; ks < ksteps - 1; ++ks) kstep(-1, false, false);
+    if (ksteps > 1) kstep(-1, false, lsteps == 0);
     if constexpr (RING) {
-      for (int64_t g = 0; g < lsteps; ++g) {
-        lstep(b);
-        b = b == kStages - 1 ? 0 : b + 1;
-      }
+      for (int g = 0; g < lsteps; ++g) lstep(g == lsteps - 1);
     }
-    // Epilogue.  Every wave has consumed the last step's stage (the barrier
-    // below), the next stage is complete and the one after is in flight.
-    const int b_last = b == 0 ? kStages - 1 : b - 1;
-    __builtin_amdgcn_sched_barrier(0);
-    barrier_no_fence();
 
+    // Epilogue.  Every wave has passed the last step's barrier, so the
+    // stage that step consumed (o_pf after the rotation) is free: the tile
+    // is staged through it before the deferred refill.  The next stage is
+    // complete and the one after is in flight.
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (!RING) {
       // LoRA-up from global memory: (alpha T / s)_hi B^T + (alpha T / s)_lo B^T.
       const int64_t mb0 = (tm * kTileM + wm * kWaveM) / 16;
@@ -451,7 +538,8 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     }
 
     // Per-token compensation scale on the fp32 accumulators.  (Tile i's
-    // scales were copied two tiles' worth of steps ago, or in the prologue.)
+    // scales were copied on the previous tile's first step, or in the
+    // prologue.)
     const char* sbuf = &lds[kScaleOff] + (i & 1) * 1024;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
@@ -464,14 +552,20 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
 
     const int64_t m0 = tm * kTileM + wm * kWaveM;
     if (N % 8 == 0) {
-      char* region = &lds[0] + b_last * kStageBytes + wave * (32 * store_pitch<kCB>());
+      char* region = &lds[0] + o_pf + wave * (32 * store_pitch<kCB>());
       store_tile_via_lds_passes<kRB, kCB, 2>(acc, region, y, M, N, m0, n0 + wn * kWaveN);
     } else {
       store_acc_bf16<kRB, kCB>(acc, y, M, N, m0, n0 + wn * kWaveN);
     }
-    // The next tile starts from stage b, complete since the last step's
-    // second barrier.
-    if (i + 1 < my_tiles) load_first(b);
+    // Every wave is done with the staging area: the deferred refill goes
+    // there.  The next tile starts from stage o_cur, complete since the
+    // last step's barrier.
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_no_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch(o_pf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < my_tiles) load_first(o_cur);
   }
   // Drain the remaining (redundant) copies before the workgroup's LDS is
   // released.

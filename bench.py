@@ -13,6 +13,14 @@ stderr.
 
 value = effective TFLOP/s = 2 M N K / (time per step): dense-equivalent
 flops, LoRA flops excluded from the numerator, LoRA time included.
+
+`detail` adds: speedups over the in-house dense GEMM and hipBLASLt; useful
+TFLOP/s (M N K + LoRA flops); per-call median / min / p90 of the step and
+its two halves; the layer without LoRA (r = 0); cold timings (MALL and L2
+flushed by a 512 MB write before every call) for the layer and both dense
+GEMMs; the graphics clock the driver reports under this load and the
+fractions of the peak rescaled to it; the standalone sparsify; CPU context
+(the oracle's selection step alone, NumPy fp32 dense GEMM).
 """
 from __future__ import annotations
 
@@ -129,6 +137,195 @@ def cpu_baseline(x, w, a, b, reps: int):
                       f"({t:.2f} s each)"}
 
 
+def cpu_context(x, w):
+    """CPU figures beside the oracle: its selection + scale step alone
+    (vectorised NumPy, one thread) on the whole X, and a plain NumPy fp32
+    dense X W^T on the host's BLAS threads."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.sparsify(x)
+        t_sel = time.perf_counter() - t0
+    xf = oracle.bf16_bits_to_f64(x).astype(np.float32)
+    wf = oracle.bf16_bits_to_f64(w).astype(np.float32)
+    xf @ wf[:64].T
+    t0 = time.perf_counter()
+    xf @ wf.T
+    t_mm = time.perf_counter() - t0
+    m, k = x.shape
+    n = w.shape[0]
+    return {"oracle_select_scale_s_1thread": round(t_sel, 3),
+            "numpy_fp32_dense_tflops": round(2.0 * m * n * k / t_mm / 1e12, 3)}
+
+
+class ClockSampler:
+    """Samples the graphics clock the driver reports (amdsmi GPU metrics,
+    one reading per XCD) from a host thread while a loop of steps runs."""
+
+    def __init__(self):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        self._th = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:          # no metrics interface: the figure is reported as null
+            log(f"[bench] no clock readings: {e!r}")
+            self._amdsmi = None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+                c = [v for v in m.get("current_gfxclks", []) if isinstance(v, (int, float))]
+                if c:
+                    self.samples.append(sum(c) / len(c))
+            except Exception:
+                pass
+            self._stop.wait(0.005)
+
+    def __enter__(self):
+        if self._amdsmi is not None:
+            import threading
+            self._th = threading.Thread(target=self._run, daemon=True)
+            self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._th is not None:
+            self._stop.set()
+            self._th.join()
+
+    def mhz(self):
+        """Median, min and max of the readings in the second half of the
+        loop (past the clock's ramp), or None.  The driver refreshes the
+        metrics every few hundred ms, so the loop runs for about a second."""
+        s = self.samples[len(self.samples) // 2:]
+        if not s:
+            return None
+        return {"median": round(statistics.median(s), 1), "min": round(min(s), 1), "max": round(max(s), 1),
+                "distinct_readings": len(set(s))}
+
+
+def dist(ms_list):
+    """median / min / p90 / mean of per-launch times, in microseconds."""
+    v = sorted(ms_list)
+    p90 = v[min(len(v) - 1, int(round(0.9 * (len(v) - 1))))]
+    return {"median": round(statistics.median(v) * 1e3, 2), "min": round(v[0] * 1e3, 2),
+            "p90": round(p90 * 1e3, 2), "mean": round(sum(v) / len(v) * 1e3, 2)}
+
+
+SUITE = ("attn_proj", "mlp_up", "mlp_down", "textimg_p05", "textimg_p10", "textimg_p25")
+
+
+def run_suite(reps: int, warmup: int):
+    """Every linear-layer workload, warm, one JSON line each: the layer
+    (pre-pass + apply), its halves, the in-house dense GEMM and hipBLASLt;
+    then Q, K and V sharing one input (one pre-pass, three applies) and the
+    time-weighted speedup over one DiT block's linears (Q, K, V, output
+    projection, MLP up, MLP down)."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gemm_token_amd as rtl
+    from workloads import gen
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def mean_ms(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {}
+    for name in SUITE:
+        cfg = gen.config(name)
+        x, w, a, b = gen.make_config(cfg)
+        xd, wd, ad, bd = up(x), up(w), up(a), up(b)
+        m, k, n, r = cfg.m, cfg.k, cfg.n, cfg.r
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((rtl.sparse_linear_workspace_bytes(m, k, r),), dtype=torch.uint8, device=dev)
+        t_layer = mean_ms(lambda: rtl.sparse_linear(xd, wd, ad, bd, 1.0, out=y, workspace=ws))
+        t_prep = mean_ms(lambda: rtl.prepare(xd, ad, 1.0, workspace=ws))
+        prep = rtl.prepare(xd, ad, 1.0, workspace=ws)
+        t_apply = mean_ms(lambda: rtl.apply(prep, wd, bd, out=y))
+        t_dense = mean_ms(lambda: rtl.dense_linear(xd, wd, out=y))
+        wt = wd.t()
+        t_blas = mean_ms(lambda: torch.matmul(xd, wt, out=y))
+        f = 2.0 * m * n * k
+        line = {"workload": name, "M": m, "K": k, "N": n, "r": r,
+                "layer_us": round(t_layer * 1e3, 2), "prepare_us": round(t_prep * 1e3, 2),
+                "apply_us": round(t_apply * 1e3, 2), "inhouse_dense_us": round(t_dense * 1e3, 2),
+                "hipblaslt_us": round(t_blas * 1e3, 2),
+                "eff_tflops": round(f / (t_layer * 1e-3) / 1e12, 1),
+                "speedup_vs_inhouse_dense": round(t_dense / t_layer, 3),
+                "speedup_vs_hipblaslt": round(t_blas / t_layer, 3)}
+        res[name] = line
+        print(json.dumps(line), flush=True)
+        del xd, wd, ad, bd, y, ws, prep
+
+    # Q, K, V: three 3072 x 3072 projections of one input sharing the
+    # LoRA-down (one pre-pass), each with its own W and LoRA-up.
+    cfg = gen.config("attn_proj")
+    x, _, a, _ = gen.make_config(cfg)
+    rng = np.random.default_rng(101)
+    ws3 = [up(gen.gaussian_bits(rng, (cfg.n, cfg.k), 0.02)) for _ in range(3)]
+    bs3 = [up(gen.gaussian_bits(rng, (cfg.n, cfg.r), 0.01)) for _ in range(3)]
+    xd, ad = up(x), up(a)
+    ys = [torch.empty((cfg.m, cfg.n), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    ws = torch.empty((rtl.sparse_linear_workspace_bytes(cfg.m, cfg.k, cfg.r),), dtype=torch.uint8, device=dev)
+
+    def qkv_sparse():
+        p = rtl.prepare(xd, ad, 1.0, workspace=ws)
+        for i in range(3):
+            rtl.apply(p, ws3[i], bs3[i], out=ys[i])
+
+    def qkv_dense():
+        for i in range(3):
+            rtl.dense_linear(xd, ws3[i], out=ys[i])
+
+    wts = [t.t() for t in ws3]
+
+    def qkv_blas():
+        for i in range(3):
+            torch.matmul(xd, wts[i], out=ys[i])
+
+    t_s, t_d, t_b = mean_ms(qkv_sparse), mean_ms(qkv_dense), mean_ms(qkv_blas)
+    qkv = {"workload": "qkv_shared_input", "M": cfg.m, "K": cfg.k, "N": f"3 x {cfg.n}", "r": cfg.r,
+           "layer_us": round(t_s * 1e3, 2), "inhouse_dense_us": round(t_d * 1e3, 2),
+           "hipblaslt_us": round(t_b * 1e3, 2),
+           "speedup_vs_inhouse_dense": round(t_d / t_s, 3), "speedup_vs_hipblaslt": round(t_b / t_s, 3)}
+    print(json.dumps(qkv), flush=True)
+
+    block = [("qkv", qkv), ("out_proj", res["attn_proj"]), ("mlp_up", res["mlp_up"]),
+             ("mlp_down", res["mlp_down"])]
+    tot_s = sum(v["layer_us"] for _, v in block)
+    tot_d = sum(v["inhouse_dense_us"] for _, v in block)
+    tot_b = sum(v["hipblaslt_us"] for _, v in block)
+    print(json.dumps({"workload": "dit_block_linears (qkv, out_proj, mlp_up, mlp_down; 4096 tokens)",
+                      "sparse_us": round(tot_s, 2), "inhouse_dense_us": round(tot_d, 2),
+                      "hipblaslt_us": round(tot_b, 2),
+                      "speedup_vs_inhouse_dense": round(tot_d / tot_s, 3),
+                      "speedup_vs_hipblaslt": round(tot_b / tot_s, 3)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +342,8 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_sparse_gemm_<workload>.json from the two rocprofv3 --pmc "
                          "output folders of --counters runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--suite", action="store_true",
+                    help="time every linear-layer workload and one DiT block's linears; one JSON line each")
     args = ap.parse_args()
     if args.traffic_from:
         t = traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload)
@@ -157,6 +356,9 @@ def main():
         print("bench.py measures one GPU: this layer runs on a single MI355X; "
               "multi-GPU runs are not part of it (see DESIGN.md on how it would shard)", file=sys.stderr)
         sys.exit(2)
+    if args.suite:
+        run_suite(args.steps, args.warmup)
+        return
 
     import numpy as np
     import torch
@@ -225,6 +427,7 @@ def main():
     torch.cuda.synchronize()
     prep_ms = [e[0].elapsed_time(e[1]) for e in ev]
     apply_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
     prep_avg = sum(prep_ms) / len(prep_ms)
     apply_avg = sum(apply_ms) / len(apply_ms)
 
@@ -233,10 +436,8 @@ def main():
     log(f"[bench] sparse step {ms_step * 1e3:.1f} us (prepare {prep_avg * 1e3:.1f} us, apply "
         f"{apply_avg * 1e3:.1f} us): {value:.1f} eff. TFLOP/s")
 
-    # In-house dense baseline and hipBLASLt (torch.matmul) for context.
-    yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-
     def time_fn(fn, reps):
+        """Mean time per call of `reps` back-to-back calls (warm)."""
         for _ in range(max(3, args.warmup)):
             fn()
         torch.cuda.synchronize()
@@ -249,6 +450,12 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    # The same layer without the LoRA branch (r = 0): the bare sparse GEMM
+    # path (pre-pass without LoRA-down, GEMM without LoRA-up).
+    r0_ms = time_fn(lambda: rtl.sparse_linear(xd, wd, None, None, 1.0, out=y, workspace=ws), args.steps)
+
+    # In-house dense baseline and hipBLASLt (torch.matmul) for context.
+    yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     dense_ms = time_fn(lambda: rtl.dense_linear(xd, wd, out=yd), args.steps)
     wt = wd.t()
     blas_ms = time_fn(lambda: torch.matmul(xd, wt, out=yd), args.steps)
@@ -259,8 +466,43 @@ def main():
     sp_ms = time_fn(lambda: lib.rtl_sparsify_2of4(xd.data_ptr(), m, k, vals.data_ptr(), idx.data_ptr(),
                                                    scale.data_ptr(), 0, stream.cuda_stream), args.steps)
     sp_bytes = 2 * m * k + m * k + m * ((k // 4 + 1) // 2) + 4 * m
-    log(f"[bench] dense in-house {dense_ms * 1e3:.1f} us, hipBLASLt {blas_ms * 1e3:.1f} us, "
-        f"sparsify {sp_ms * 1e3:.1f} us")
+    log(f"[bench] r=0 {r0_ms * 1e3:.1f} us, dense in-house {dense_ms * 1e3:.1f} us, hipBLASLt "
+        f"{blas_ms * 1e3:.1f} us, sparsify {sp_ms * 1e3:.1f} us")
+
+    # Cold: the MALL (256 MB) and the L2s flushed before every call by
+    # writing 512 MB; events around the call only.
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+
+    def time_cold(fn, reps=30):
+        out = []
+        for i in range(reps):
+            flush.fill_(i & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return dist(out)
+
+    cold_step = time_cold(step)
+    cold_dense = time_cold(lambda: rtl.dense_linear(xd, wd, out=yd))
+    cold_blas = time_cold(lambda: torch.matmul(xd, wt, out=yd))
+    del flush
+
+    # Graphics clock under this load, read from the driver while ~1 s of
+    # steps runs; the peaks rescaled to it say how much of the gap to the
+    # nominal 2.4 GHz peak is the clock.
+    for _ in range(200):
+        step()
+    with ClockSampler() as clk:
+        for _ in range(max(1, int(1.0 / (ms_step * 1e-3)))):
+            step()
+        torch.cuda.synchronize()
+    sclk_obs = clk.mhz()
+    sclk = sclk_obs["median"] if sclk_obs else None
+    log(f"[bench] cold step {cold_step['median']} us, dense {cold_dense['median']} us; sclk {sclk_obs} MHz")
 
     # Roofline of the dominant kernel: the structured-sparse GEMM (apply).
     # Algorithmic flops per launch: the kept half of the product, M N K
@@ -272,10 +514,14 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_DENSE_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_DENSE_TFLOPS, 4),
                 "traffic": traffic["hbm_bytes_per_launch"] if traffic else None}
+    useful_flops = float(m) * n * k + 2.0 * m * k * r + 2.0 * m * n * r
 
     cpu = None
+    cpu_ctx = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, w, a, b, args.cpu_reps)
+        cpu_ctx = cpu_context(x, w)
+    peak_at_sclk = PEAK_BF16_DENSE_TFLOPS * sclk / 2400.0 if sclk else None
 
     out = {
         "metric": METRIC,
@@ -307,6 +553,24 @@ def main():
             "sparsify_2of4_us": round(sp_ms * 1e3, 2),
             "sparsify_2of4_GBs": round(sp_bytes / (sp_ms * 1e-3) / 1e9, 1),
             "sparsify_2of4_frac_hbm": round(sp_bytes / (sp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "useful_tflops": round(useful_flops / (ms_step * 1e-3) / 1e12, 1),
+            "step_us_per_call": dist(step_ms),
+            "prepare_us_per_call": dist(prep_ms),
+            "apply_us_per_call": dist(apply_ms),
+            "r0_step_us": round(r0_ms * 1e3, 2),
+            "r0_eff_tflops": round(flops_dense_eq / (r0_ms * 1e-3) / 1e12, 1),
+            "r0_speedup_vs_inhouse_dense": round(dense_ms / r0_ms, 3),
+            "r0_speedup_vs_hipblaslt": round(blas_ms / r0_ms, 3),
+            "sparsify_over_sparse_linear": round(sp_ms / ms_step, 4),
+            "cold_step_us": cold_step,
+            "cold_inhouse_dense_us": cold_dense,
+            "cold_hipblaslt_us": cold_blas,
+            "cold_speedup_vs_inhouse_dense": round(cold_dense["median"] / cold_step["median"], 3),
+            "cold_speedup_vs_hipblaslt": round(cold_blas["median"] / cold_step["median"], 3),
+            "sclk_mhz_observed": sclk_obs,
+            "frac_dense_peak_at_sclk": round(value / peak_at_sclk, 4) if sclk else None,
+            "apply_frac_peak_at_sclk": round(achieved / peak_at_sclk, 4) if sclk else None,
+            "cpu_context": cpu_ctx,
             "kernel_source_hash": kernel_source_hash(),
         },
     }
