@@ -62,6 +62,24 @@ __device__ __forceinline__ void select_quad(const uint32_t (&w)[8], Quad& q, flo
   }
 }
 
+// The kept half only (the pre-pass with DMA-streamed operands forms the
+// LoRA-down from the whole input words instead of the pruned half): kept
+// operand words and their 16-bit index field; both L1 sums as above.
+__device__ __forceinline__ void select_quad_kept(const uint32_t (&w)[8], u32x4& kept, uint32_t& kcode,
+                                                 float& lk, float& lp) {
+  kcode = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t lo = w[2 * g], hi = w[2 * g + 1];
+    const Group4 r = rank_group(lo, hi);
+    const uint32_t ks = pair_selector_sorted(r.first, r.second);
+    kept[g] = __builtin_amdgcn_perm(hi, lo, ks);
+    kcode |= code_from_selector(ks) << (4 * g);
+    lk = add_mag_pair(lk, r.first, r.second);
+    lp = add_mag_pair(lp, r.third, r.fourth);
+  }
+}
+
 // The loads below go through buffer resources: a guarded element is given
 // an offset past the end of the tensor and reads as zero, so no load sits
 // behind a branch and the compiler can issue them all before waiting.
@@ -279,11 +297,12 @@ constexpr int kXStages = 8, kXAhead = 7;
 constexpr int kAStages = 3, kAAhead = 2;
 
 // NI 1-KiB copies (8 rows x 128 bytes each): instruction i writes LDS
-// lds_addr + 1024 i (through M0) from per-lane source offsets v[i].  No
-// output registers, M0 saved and restored, no SCC write (as the GEMM's copy
-// blocks).
+// lds_addr + 1024 i (through M0) from per-lane source offsets v[i] plus the
+// scalar offset soff.  No output registers, M0 saved and restored, one wait
+// state between each M0 write and the copy that reads it; the M0 values
+// come from SGPRs (no SCC write).
 template <int NI>
-__device__ __forceinline__ void dma_rows_asm(__amdgpu_buffer_rsrc_t rs, const uint32_t (&v)[NI],
+__device__ __forceinline__ void dma_rows_asm(__amdgpu_buffer_rsrc_t rs, const uint32_t (&v)[NI], uint32_t soff,
                                              uint32_t lds_addr) {
   uint32_t saved;
   if constexpr (NI == 2) {
@@ -291,29 +310,37 @@ __device__ __forceinline__ void dma_rows_asm(__amdgpu_buffer_rsrc_t rs, const ui
         "s_nop 4\n\t"
         "s_mov_b32 %[sv], m0\n\t"
         "s_mov_b32 m0, %[l0]\n\t"
-        "buffer_load_dwordx4 %[v0], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v0], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l1]\n\t"
-        "buffer_load_dwordx4 %[v1], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v1], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[sv]"
         : [sv] "=&s"(saved)
-        : [v0] "v"(v[0]), [v1] "v"(v[1]), [rs] "s"(rs), [l0] "s"(lds_addr), [l1] "s"(lds_addr + 0x400u)
+        : [v0] "v"(v[0]), [v1] "v"(v[1]), [rs] "s"(rs), [so] "s"(soff), [l0] "s"(lds_addr),
+          [l1] "s"(lds_addr + 0x400u)
         : "memory");
   } else if constexpr (NI == 4) {
     asm volatile(
         "s_nop 4\n\t"
         "s_mov_b32 %[sv], m0\n\t"
         "s_mov_b32 m0, %[l0]\n\t"
-        "buffer_load_dwordx4 %[v0], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v0], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l1]\n\t"
-        "buffer_load_dwordx4 %[v1], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v1], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l2]\n\t"
-        "buffer_load_dwordx4 %[v2], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v2], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l3]\n\t"
-        "buffer_load_dwordx4 %[v3], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v3], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[sv]"
         : [sv] "=&s"(saved)
-        : [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [rs] "s"(rs), [l0] "s"(lds_addr),
-          [l1] "s"(lds_addr + 0x400u), [l2] "s"(lds_addr + 0x800u), [l3] "s"(lds_addr + 0xc00u)
+        : [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [rs] "s"(rs), [so] "s"(soff),
+          [l0] "s"(lds_addr), [l1] "s"(lds_addr + 0x400u), [l2] "s"(lds_addr + 0x800u),
+          [l3] "s"(lds_addr + 0xc00u)
         : "memory");
   } else {
     static_assert(NI == 8, "2, 4 or 8 row blocks");
@@ -321,27 +348,36 @@ __device__ __forceinline__ void dma_rows_asm(__amdgpu_buffer_rsrc_t rs, const ui
         "s_nop 4\n\t"
         "s_mov_b32 %[sv], m0\n\t"
         "s_mov_b32 m0, %[l0]\n\t"
-        "buffer_load_dwordx4 %[v0], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v0], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l1]\n\t"
-        "buffer_load_dwordx4 %[v1], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v1], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l2]\n\t"
-        "buffer_load_dwordx4 %[v2], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v2], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l3]\n\t"
-        "buffer_load_dwordx4 %[v3], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v3], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l4]\n\t"
-        "buffer_load_dwordx4 %[v4], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v4], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l5]\n\t"
-        "buffer_load_dwordx4 %[v5], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v5], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l6]\n\t"
-        "buffer_load_dwordx4 %[v6], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v6], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l7]\n\t"
-        "buffer_load_dwordx4 %[v7], %[rs], 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[v7], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[sv]"
         : [sv] "=&s"(saved)
         : [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [v4] "v"(v[4]), [v5] "v"(v[5]),
-          [v6] "v"(v[6]), [v7] "v"(v[7]), [rs] "s"(rs), [l0] "s"(lds_addr), [l1] "s"(lds_addr + 0x400u),
-          [l2] "s"(lds_addr + 0x800u), [l3] "s"(lds_addr + 0xc00u), [l4] "s"(lds_addr + 0x1000u),
-          [l5] "s"(lds_addr + 0x1400u), [l6] "s"(lds_addr + 0x1800u), [l7] "s"(lds_addr + 0x1c00u)
+          [v6] "v"(v[6]), [v7] "v"(v[7]), [rs] "s"(rs), [so] "s"(soff), [l0] "s"(lds_addr),
+          [l1] "s"(lds_addr + 0x400u), [l2] "s"(lds_addr + 0x800u), [l3] "s"(lds_addr + 0xc00u),
+          [l4] "s"(lds_addr + 0x1000u), [l5] "s"(lds_addr + 0x1400u), [l6] "s"(lds_addr + 0x1800u),
+          [l7] "s"(lds_addr + 0x1c00u)
         : "memory");
   }
   (void)saved;
@@ -365,7 +401,17 @@ __device__ __forceinline__ void rows_offsets(int64_t row0, int64_t rows, int64_t
 // Byte offset, inside a swizzled tile (128-byte rows), of chunk c of row n.
 __device__ __forceinline__ uint32_t swz(int n, int c) { return (uint32_t)(n * 128 + ((c ^ (n & 7)) << 4)); }
 
-template <int NCB>
+// LoRA-down here: T = X A^T - s (M*X) A^T, the first product by dense
+// 16x16x32 MFMAs on the input words as they are, the second by the
+// structured-sparse MFMA on the kept half (the same operand the GEMM gets).
+// Both accumulate in fp32; the difference loses at most a few units in the
+// last place of |X A^T|, far below the rounding of the output.  The L1 sums
+// still come from the exact kept and pruned magnitudes.
+//
+// FULLK (K % 128 == 0, every k-step inside K): the copy and store offsets
+// are computed once and advanced by a scalar offset per step; otherwise
+// they are recomputed per step with the channel-tail guards.
+template <int NCB, bool FULLK>
 __global__ void __launch_bounds__(64 * kDWaves, 1)
 prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora_a,
                    int64_t M, int64_t K, int64_t r, float alpha,
@@ -397,47 +443,87 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, M * K * 2);
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(lora_a, r * K * 2);
-  const int64_t ks_begin = wave * ksteps / kDWaves, ks_end = (wave + 1) * ksteps / kDWaves;
-  const int64_t nks = ks_end - ks_begin;             // uniform per wavefront
+  // The compressed operand and its position fields of the whole padded
+  // workspace (ngroups groups of 8 blocks, ksteps steps).
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(xv, ngroups * ksteps * 8192);
+  const __amdgpu_buffer_rsrc_t ir = make_rsrc(xi, ngroups * ksteps * 1024);
+  const int ks_begin = (int)(wave * ksteps / kDWaves), ks_end = (int)((wave + 1) * ksteps / kDWaves);
+  const int nks = ks_end - ks_begin;                  // uniform per wavefront
   char* const ring = lds + wave * kWaveBytes;
   const uint32_t ring_addr = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(ring));
+
+  // FULLK: per-lane source offsets at the wavefront's first k-step; a row
+  // past the tensor gets 0x80000000, which stays past its end (< 2 GiB)
+  // whatever scalar offset is added.
+  uint32_t vx[kXOps], va[kAOps];
+  if constexpr (FULLK) {
+    const int64_t kl = (int64_t)ks_begin * 64 + 8 * ((lane & 7) ^ (lane >> 3));
+#pragma unroll
+    for (int i = 0; i < kXOps; ++i) {
+      const int64_t rw = mb * 16 + 8 * i + (lane >> 3);
+      vx[i] = rw < M ? (uint32_t)((rw * K + kl) * 2) : 0x80000000u;
+    }
+#pragma unroll
+    for (int i = 0; i < kAOps; ++i) {
+      const int64_t rw = 8 * i + (lane >> 3);
+      va[i] = rw < r ? (uint32_t)((rw * K + kl) * 2) : 0x80000000u;
+    }
+  }
 
   // Copies issued together: A of step t_a (if t_a >= 0) first, then X of
   // step t_x, each clamped to the wavefront's last step (a harmless repeat
   // into a stage nobody reads again).  A goes first so that waiting for
   // A(t) -- with in-order completion -- does not also wait for the X copy
   // issued far ahead alongside it.
-  auto copy_step = [&](int64_t t_x, int64_t t_a) {
+  auto copy_step = [&](int t_x, int t_a) {
     if (t_a >= 0) {
-      const int64_t tc = t_a < nks ? t_a : nks - 1;
-      uint32_t v[kAOps];
-      rows_offsets<kAOps>(0, r, K, (ks_begin + tc) * 64, v);
-      dma_rows_asm<kAOps>(ar, v, ring_addr + kXStages * kXBytes + (uint32_t)(t_a % kAStages) * kABytes);
+      const int tc = t_a < nks ? t_a : nks - 1;
+      const uint32_t dst = ring_addr + kXStages * kXBytes + (uint32_t)(t_a % kAStages) * kABytes;
+      if constexpr (FULLK) {
+        dma_rows_asm<kAOps>(ar, va, __builtin_amdgcn_readfirstlane(128u * (uint32_t)tc), dst);
+      } else {
+        uint32_t v[kAOps];
+        rows_offsets<kAOps>(0, r, K, (int64_t)(ks_begin + tc) * 64, v);
+        dma_rows_asm<kAOps>(ar, v, 0u, dst);
+      }
     }
-    const int64_t tc = t_x < nks ? t_x : nks - 1;
-    uint32_t v[kXOps];
-    rows_offsets<kXOps>(mb * 16, M, K, (ks_begin + tc) * 64, v);
-    dma_rows_asm<kXOps>(xr, v, ring_addr + (uint32_t)(t_x % kXStages) * kXBytes);
+    const int tc = t_x < nks ? t_x : nks - 1;
+    const uint32_t dst = ring_addr + (uint32_t)(t_x % kXStages) * kXBytes;
+    if constexpr (FULLK) {
+      dma_rows_asm<kXOps>(xr, vx, __builtin_amdgcn_readfirstlane(128u * (uint32_t)tc), dst);
+    } else {
+      uint32_t v[kXOps];
+      rows_offsets<kXOps>(mb * 16, M, K, (int64_t)(ks_begin + tc) * 64, v);
+      dma_rows_asm<kXOps>(xr, v, 0u, dst);
+    }
   };
 
   float lk = 0.f, lp = 0.f;
-  f32x4 tk[NCB], tp[NCB];
+  f32x4 tk[NCB], tx[NCB];
 #pragma unroll
-  for (int c = 0; c < NCB; ++c) { tk[c] = (f32x4){0, 0, 0, 0}; tp[c] = (f32x4){0, 0, 0, 0}; }
+  for (int c = 0; c < NCB; ++c) { tk[c] = (f32x4){0, 0, 0, 0}; tx[c] = (f32x4){0, 0, 0, 0}; }
 
-  // Lane l: token l % 16, channels 16 (l / 16) + [0, 16) = chunks 2q, 2q + 1;
-  // B operand halves of rank row l % 16: chunks l / 16 and 4 + l / 16.
+  // Lane l: token l % 16, channels 16 (l / 16) + [0, 16) = chunks 2q, 2q + 1
+  // (selection and the structured-sparse operand); chunks q and 4 + q of
+  // the token (dense A operands of the two 32-channel halves) and of rank
+  // row l % 16 (the B operand halves of both instructions).
   const int tok = lane & 15, q = lane >> 4;
   const uint32_t xo0 = swz(tok, 2 * q), xo1 = swz(tok, 2 * q + 1);
+  const uint32_t xd0 = swz(tok, q), xd1 = swz(tok, 4 + q);
   const uint32_t bo0 = swz(tok, q), bo1 = swz(tok, 4 + q);
+  // Store offsets: the k-step's 1 KiB of operand words for this 16-token
+  // block (lane's 16 bytes) and 16-bit position field; per step they move
+  // by 8 KiB and 1 KiB.
+  const uint32_t sv0 = (uint32_t)((((grp * ksteps + ks_begin) * 8 + sub) * 64 + lane) * 16);
+  const uint32_t si0 = (uint32_t)((((grp * ksteps + ks_begin) * 64 + lane) * 8 + sub) * 2);
 
   if (nks > 0) {
     // Prologue in the steady-state issue order: step t issues A(t + 2), then
     // X(t + 7); X(0..4) first, then (A(0), X(5)), (A(1), X(6)).
     for (int i = 0; i < kXAhead - kAAhead; ++i) copy_step(i, -1);
     for (int i = 0; i < kAAhead; ++i) copy_step(kXAhead - kAAhead + i, i);
-    for (int64_t t = 0; t < nks; ++t) {
+    for (int t = 0; t < nks; ++t) {
       __builtin_amdgcn_sched_barrier(0);
       copy_step(t + kXAhead, t + kAAhead);
       // Wait for step t's copies (X(t) was issued before A(t)).  Younger
@@ -453,20 +539,25 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
       const char* xs = ring + (t % kXStages) * kXBytes;
       const u32x4 c0 = *reinterpret_cast<const u32x4*>(xs + xo0);
       const u32x4 c1 = *reinterpret_cast<const u32x4*>(xs + xo1);
+      const u32x4 d0 = *reinterpret_cast<const u32x4*>(xs + xd0);
+      const u32x4 d1 = *reinterpret_cast<const u32x4*>(xs + xd1);
       const uint32_t w[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-      Quad qd;
-      select_quad(w, qd, lk, lp);
-      const int64_t kst = ks_begin + t;
-      xv[((grp * ksteps + kst) * 8 + sub) * 64 + lane] = qd.kept;
-      xi[((grp * ksteps + kst) * 64 + lane) * 8 + sub] = (uint16_t)qd.kcode;
+      u32x4 kept;
+      uint32_t kcode;
+      select_quad_kept(w, kept, kcode, lk, lp);
+      const uint32_t so_v = __builtin_amdgcn_readfirstlane(8192u * (uint32_t)t);
+      const uint32_t so_i = __builtin_amdgcn_readfirstlane(1024u * (uint32_t)t);
+      __builtin_amdgcn_raw_buffer_store_b128(kept, vr, sv0, so_v, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)kcode, ir, si0, so_i, 0);
       const char* as = ring + kXStages * kXBytes + (t % kAStages) * kABytes;
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(as + c * 2048 + bo0);
         const u32x4 b1 = *reinterpret_cast<const u32x4*>(as + c * 2048 + bo1);
         const bf16x16 bf = __builtin_bit_cast(bf16x16, (u32x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
-        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, qd.kept), bf, tk[c], (int)qd.kcode, 0, 0);
-        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, qd.pruned), bf, tp[c], (int)qd.pcode, 0, 0);
+        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, kept), bf, tk[c], (int)kcode, 0, 0);
+        tx[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, d0), __builtin_bit_cast(bf16x8, b0), tx[c], 0, 0, 0);
+        tx[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, d1), __builtin_bit_cast(bf16x8, b1), tx[c], 0, 0, 0);
       }
     }
   }
@@ -493,14 +584,14 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
   }
   __syncthreads();
   // Accumulator layout of a 16x16 block: lane l holds column l % 16 of rows
-  // 4 (l / 16) + i.  T_w = T_pruned + (1 - s) T_kept per wavefront, then
+  // 4 (l / 16) + i.  T_w = (X A^T)_w - s (M*X A^T)_w per wavefront, then
   // summed over wavefronts in a fixed order.
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = 4 * (lane >> 4) + i;
-      red.t[wave][rr][c * 16 + (lane & 15)] = tp[c][i] + (1.0f - red.s[rr]) * tk[c][i];
+      red.t[wave][rr][c * 16 + (lane & 15)] = tx[c][i] - red.s[rr] * tk[c][i];
     }
   }
   __syncthreads();
@@ -548,12 +639,15 @@ hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M
     // 16-token block (same grid and mapping).
     const dim3 dblock(64 * kDWaves);
     const int64_t ksteps = L.kp / 64;
+    const bool full = K % 128 == 0;
     if (r > 0 && ncb <= 2) {
-      prepass_dma_kernel<2><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
+      if (full) prepass_dma_kernel<2, true><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
+      else prepass_dma_kernel<2, false><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
       return hipGetLastError();
     }
     if (r > 0 && ncb <= 4) {
-      prepass_dma_kernel<4><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
+      if (full) prepass_dma_kernel<4, true><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
+      else prepass_dma_kernel<4, false><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
       return hipGetLastError();
     }
   }
