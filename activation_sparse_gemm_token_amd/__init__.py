@@ -24,7 +24,7 @@ import os
 __all__ = [
     "RtlError", "lib", "library_path", "sparsify_2of4", "sparse_linear", "dense_linear",
     "sparse_linear_workspace_bytes", "version", "status_string", "STATUS", "prepare", "apply", "Prepared",
-    "FOLD_SCALE", "MAX_LORA_RANK",
+    "FOLD_SCALE", "MAX_LORA_RANK", "sparse_linear_compressed",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +49,8 @@ _SIGNATURES = {
                                                  ctypes.c_size_t, _c_vp]),
     "rtl_sparse_linear_apply": (ctypes.c_int, [_c_vp, ctypes.c_size_t, _c_vp, _c_vp, _c_i64, _c_i64,
                                                _c_i64, _c_i64, _c_vp, _c_vp]),
+    "rtl_sparse_linear_compressed": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                                                    _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "rtl_dense_linear": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
     "rtl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rtl_version": (ctypes.c_int, []),
@@ -214,6 +216,34 @@ def apply(prep: Prepared, w, lora_b=None, out=None):
                                        y.data_ptr(), _stream())
     _check(st, "rtl_sparse_linear_apply")
     return y.reshape(*prep.lead_shape, n)
+
+
+def sparse_linear_compressed(vals, idx, scale, w, out=None, workspace=None):
+    """Y = scale * (decompress(vals, idx) W^T) for an activation compressed by
+    ``sparsify_2of4`` (vals [M, K/2] bf16, idx [M, ceil(K/8)] uint8, scale [M]
+    fp32 or None), w [N, K] bf16.  Returns y [M, N] bf16."""
+    torch = _torch()
+    v2 = _as_2d(vals, "vals")
+    w2 = _as_2d(w, "w")
+    m = v2.shape[0]
+    n, k = w2.shape
+    if v2.shape[1] * 2 != k:
+        raise ValueError(f"vals has {v2.shape[1]} columns, w has {k} input channels")
+    if idx.dtype != torch.uint8 or not idx.is_cuda or not idx.is_contiguous() or \
+            tuple(idx.shape) != (m, (k // 4 + 1) // 2):
+        raise ValueError("idx must be a contiguous uint8 device tensor [M, ceil(K/8)]")
+    if scale is not None and (scale.dtype != torch.float32 or not scale.is_cuda or scale.numel() != m):
+        raise ValueError("scale must be a float32 device tensor [M] or None")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=w2.device)
+    need = sparse_linear_workspace_bytes(m, k, 0)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=w2.device)
+    st = lib().rtl_sparse_linear_compressed(v2.data_ptr(), idx.data_ptr(),
+                                            scale.data_ptr() if scale is not None else None,
+                                            w2.data_ptr(), m, n, k, y.data_ptr(), workspace.data_ptr(),
+                                            workspace.numel(), _stream())
+    _check(st, "rtl_sparse_linear_compressed")
+    return y
 
 
 def dense_linear(x, w, out=None):

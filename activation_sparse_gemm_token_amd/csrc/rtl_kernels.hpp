@@ -24,4 +24,9 @@ hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const ui
 hipError_t launch_dense_gemm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                              int64_t K, uint16_t* y, hipStream_t stream);
 
+// Canonical compressed activation (vals, idx, scale or null) into the
+// workspace regions of ws_layout(M, K, 0).
+hipError_t launch_repack(const uint16_t* vals, const uint8_t* idx, const float* scale, int64_t M,
+                         int64_t K, void* workspace, hipStream_t stream);
+
 }  // namespace rtl

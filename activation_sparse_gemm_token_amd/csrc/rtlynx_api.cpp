@@ -162,6 +162,27 @@ RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const
   return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y, cus, stream));
 }
 
+RTL_API rtl_status rtl_sparse_linear_compressed(const uint16_t* vals, const uint8_t* idx, const float* scale,
+                                                const uint16_t* w, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                                                void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!dims_ok(M, K) || N < 0 || N >= kMaxDim) return RTL_ERR_BAD_SHAPE;
+  if (!layer_sizes_ok(M, N, K, 0)) return RTL_ERR_BAD_SHAPE;
+  if (M == 0 || N == 0) return RTL_OK;
+  if (vals == nullptr || idx == nullptr || w == nullptr || y == nullptr) return RTL_ERR_NULL_POINTER;
+  if (!aligned16(vals) || !aligned16(idx) || !aligned16(w) || !aligned16(y) ||
+      (scale != nullptr && !aligned16(scale)))
+    return RTL_ERR_MISALIGNED;
+  if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, 0).total) return RTL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
+  int cus = 0;
+  const rtl_status d = check_device(&cus);
+  if (d != RTL_OK) return d;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const hipError_t e = rtl::launch_repack(vals, idx, scale, M, K, workspace, stream);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(rtl::launch_sparse_gemm(workspace, w, nullptr, M, N, K, 0, y, cus, stream));
+}
+
 RTL_API rtl_status rtl_dense_linear(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                                     int64_t K, uint16_t* y, void* hip_stream) {
   if (!dims_ok(M, K) || N < 0 || N >= kMaxDim) return RTL_ERR_BAD_SHAPE;

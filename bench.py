@@ -16,7 +16,8 @@ flops, LoRA flops excluded from the numerator, LoRA time included.
 
 `detail` adds: speedups over the in-house dense GEMM and hipBLASLt; useful
 TFLOP/s (M N K + LoRA flops); per-call median / min / p90 of the step and
-its two halves; the layer without LoRA (r = 0); cold timings (MALL and L2
+its two halves; the layer without LoRA (r = 0) and its unfused form
+(rtl_sparsify_2of4, then rtl_sparse_linear_compressed); cold timings (MALL and L2
 flushed by a 512 MB write before every call) for the layer and both dense
 GEMMs; the graphics clock the driver reports under this load and the
 fractions of the peak rescaled to it; the standalone sparsify; CPU context
@@ -466,8 +467,22 @@ def main():
     sp_ms = time_fn(lambda: lib.rtl_sparsify_2of4(xd.data_ptr(), m, k, vals.data_ptr(), idx.data_ptr(),
                                                    scale.data_ptr(), 0, stream.cuda_stream), args.steps)
     sp_bytes = 2 * m * k + m * k + m * ((k // 4 + 1) // 2) + 4 * m
+    # The unfused form of the layer without LoRA: sparsify to the canonical
+    # compressed X in HBM, then the GEMM on it (its repack included).
+    ws0 = torch.empty((rtl.sparse_linear_workspace_bytes(m, k, 0),), dtype=torch.uint8, device=dev)
+
+    def unfused():
+        lib.rtl_sparsify_2of4(xd.data_ptr(), m, k, vals.data_ptr(), idx.data_ptr(), scale.data_ptr(), 0,
+                              stream.cuda_stream)
+        lib.rtl_sparse_linear_compressed(vals.data_ptr(), idx.data_ptr(), scale.data_ptr(), wd.data_ptr(),
+                                         m, n, k, y.data_ptr(), ws0.data_ptr(), ws0.numel(), stream.cuda_stream)
+
+    unf_ms = time_fn(unfused, args.steps)
+    comp_ms = time_fn(lambda: lib.rtl_sparse_linear_compressed(
+        vals.data_ptr(), idx.data_ptr(), scale.data_ptr(), wd.data_ptr(), m, n, k, y.data_ptr(),
+        ws0.data_ptr(), ws0.numel(), stream.cuda_stream), args.steps)
     log(f"[bench] r=0 {r0_ms * 1e3:.1f} us, dense in-house {dense_ms * 1e3:.1f} us, hipBLASLt "
-        f"{blas_ms * 1e3:.1f} us, sparsify {sp_ms * 1e3:.1f} us")
+        f"{blas_ms * 1e3:.1f} us, sparsify {sp_ms * 1e3:.1f} us, unfused {unf_ms * 1e3:.1f} us")
 
     # Cold: the MALL (256 MB) and the L2s flushed before every call by
     # writing 512 MB; events around the call only.
@@ -562,6 +577,9 @@ def main():
             "r0_speedup_vs_inhouse_dense": round(dense_ms / r0_ms, 3),
             "r0_speedup_vs_hipblaslt": round(blas_ms / r0_ms, 3),
             "sparsify_over_sparse_linear": round(sp_ms / ms_step, 4),
+            "unfused_r0_us": round(unf_ms * 1e3, 2),
+            "compressed_gemm_us": round(comp_ms * 1e3, 2),
+            "unfused_over_fused_r0": round(unf_ms / r0_ms, 4),
             "cold_step_us": cold_step,
             "cold_inhouse_dense_us": cold_dense,
             "cold_hipblaslt_us": cold_blas,

@@ -160,6 +160,36 @@ rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspace_bytes
                                    uint16_t* y, void* hip_stream);
 
 /*
+ * rtl_sparse_linear_compressed - the structured-sparse GEMM on an activation
+ * already compressed in the canonical format of rtl_sparsify_2of4 (compress
+ * once, multiply by any number of weights; also the unfused form of the layer,
+ * sparsify then GEMM, that the qingkeai article, section 04, contrasts with
+ * the fused kernel):
+ *
+ *   y = bf16( scale[m] * sum_k decompress(vals, idx)[m, k] * w[n, k] )
+ *
+ *   vals   [M, K/2] bf16, idx [M, ceil(K/8)] bytes: exactly as rtl_sparsify_2of4
+ *          writes them (idx nibble idx0 | idx1 << 2, idx0 < idx1, even group
+ *          in the low nibble; the values multiply W at channels 4g + idx0 and
+ *          4g + idx1 of group g).
+ *   scale  [M] fp32 per-token factor applied to the fp32 accumulators, or NULL
+ *          for 1 (e.g. values stored with RTL_FOLD_SCALE).
+ *   w      [N, K] bf16, y [M, N] bf16 (outputs; caller-owned device memory).
+ *   workspace  device memory of rtl_sparse_linear_workspace_bytes(M, K, 0)
+ *          bytes, overwritten (the operand reordered for the matrix cores).
+ *
+ * There is no LoRA branch (the canonical format carries no LoRA-down).  Same
+ * shape, alignment, ownership, stream and error rules as rtl_sparse_linear
+ * (r = 0); a code of 0 in idx is accepted (both positions 0) and contributes
+ * whatever its two values give.
+ */
+rtl_status rtl_sparse_linear_compressed(const uint16_t* vals, const uint8_t* idx,
+                                        const float* scale, const uint16_t* w,
+                                        int64_t M, int64_t N, int64_t K, uint16_t* y,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* hip_stream);
+
+/*
  * rtl_dense_linear - the dense baseline Y = X W^T (the denominator of the
  * speedups the pages quote, qingkeai article, section 05), bf16 inputs, fp32
  * accumulation on the dense matrix cores, bf16 output rounded to nearest even.

@@ -26,4 +26,5 @@ from .rtlynx_ref import (  # noqa: F401
     sparse_linear_ref,
     sparse_linear_gather_ref,
     lora_down_ref,
+    compressed_linear_ref,
 )

@@ -256,3 +256,17 @@ def sparse_linear_gather_ref(x_bits, w_bits, a_bits=None, b_bits=None, alpha: fl
     if a_bits is not None and b_bits is not None and np.asarray(a_bits).shape[0] > 0:
         y = y + alpha * (lora_down_ref(x_bits, a_bits) @ bf16_bits_to_f64(b_bits).T)
     return y
+
+
+def compressed_linear_ref(vals, idx, scale, w_bits, k: int) -> np.ndarray:
+    """The structured-sparse product on an activation already in the
+    canonical compressed form: Y = diag(scale) decompress(vals, idx) W^T in
+    fp64 (qingkeai article, section 04: the sparse GEMM consumes the
+    compressed activation; section 02: Y = S(X) W^T with the compensation as
+    a per-token factor).  ``scale`` None means 1 (values stored already
+    scaled)."""
+    xd = bf16_bits_to_f64(decompress(vals, idx, k))
+    y = xd @ bf16_bits_to_f64(w_bits).T
+    if scale is not None:
+        y = y * np.asarray(scale, dtype=np.float64)[:, None]
+    return y

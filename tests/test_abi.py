@@ -201,3 +201,28 @@ def test_prepare_apply_without_device():
     assert _pr() == NODEV
     assert _ap() == NODEV
     assert _pr(r=0, a=None) == NODEV
+
+
+def _cl(v=P, i=P2, s=P3, w=P4, m=64, n=128, k=256, y=P5, ws=WSP, wsb=BIG, stream=None):
+    return rtl.lib().rtl_sparse_linear_compressed(v, i, s, w, m, n, k, y, ws, wsb, stream)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=6), SHAPE), (dict(k=0), SHAPE), (dict(m=-1), SHAPE), (dict(n=-1), SHAPE),
+    (dict(v=None), NULLP), (dict(i=None), NULLP), (dict(w=None), NULLP), (dict(y=None), NULLP),
+    (dict(v=P + 8), MISAL), (dict(i=P2 + 1), MISAL), (dict(s=P3 + 4), MISAL), (dict(w=P4 + 8), MISAL),
+    (dict(y=P5 + 2), MISAL), (dict(ws=None), WS), (dict(wsb=16), WS), (dict(ws=WSP + 4), MISAL),
+    (dict(m=0), OK), (dict(n=0), OK), (dict(m=1 << 15, n=1 << 15), SHAPE),
+])
+def test_compressed_rejects_invalid_arguments(kw, status):
+    assert _cl(**kw) == status
+
+
+def test_compressed_without_device():
+    if not _no_gpu():
+        pytest.skip("a GPU is present")
+    assert _cl() == NODEV
+    assert _cl(s=None) == NODEV           # no scale: s = 1
+    need = rtl.lib().rtl_sparse_linear_workspace_bytes(64, 256, 0)
+    assert _cl(wsb=need) == NODEV
+    assert _cl(wsb=need - 1) == WS

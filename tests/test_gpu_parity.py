@@ -242,3 +242,58 @@ def test_prepare_once_apply_many():
         y2 = to_host(rtl.sparse_linear(xd, to_dev(w), ad, to_dev(b), lora_scale=0.5))
         assert np.array_equal(y1, y2)
         assert_y_close(oracle.bf16_bits_to_f64(y1), oracle.sparse_linear_ref(x, w, a, b, 0.5), f"apply N={n}")
+
+
+COMPRESSED_SHAPES = [
+    # (M, K, N): K % 16 == 0, == 4, == 8, == 12; ragged M and N; one group; many tiles
+    (64, 256, 128), (300, 516, 200), (257, 1000, 333), (1, 4, 1), (5, 12, 7), (33, 260, 300),
+    (512, 3072, 520),
+]
+
+
+@pytest.mark.parametrize("shape", COMPRESSED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_compressed_linear_small_and_ragged(shape):
+    """rtl_sparse_linear_compressed on the oracle's canonical compressed form,
+    with and without the per-token scale."""
+    m, k, n = shape
+    say(f"[parity] compressed M={m} K={k} N={n}")
+    rng = np.random.default_rng(m * 7 + k + n)
+    x = gen.mixture_bernoulli(rng, m, k)
+    w = gen.gaussian_bits(rng, (n, k), 0.02)
+    _, _, s, i0, i1 = oracle.sparsify(x)
+    vals, idx = oracle.compress(x, i0, i1)
+    s32 = s.astype(np.float32)
+    vd = to_dev(vals)
+    id_ = torch.from_numpy(idx).to(DEV)
+    wd = to_dev(w)
+    y = rtl.sparse_linear_compressed(vd, id_, torch.from_numpy(s32).to(DEV), wd)
+    y0 = rtl.sparse_linear_compressed(vd, id_, None, wd)
+    torch.cuda.synchronize()
+    assert_y_close(y_to_f64(y), oracle.compressed_linear_ref(vals, idx, s32, w, k), f"compressed {shape}")
+    assert_y_close(y_to_f64(y0), oracle.compressed_linear_ref(vals, idx, None, w, k), f"compressed {shape}, no scale")
+
+
+def test_unfused_sparsify_then_compressed_gemm():
+    """The unfused form of the layer without LoRA: rtl_sparsify_2of4 writes
+    the canonical compressed X, rtl_sparse_linear_compressed multiplies it;
+    the result is the layer (r = 0) within the output bar."""
+    for name, m in (("attn_proj", 512), ("mlp_down", 256)):
+        x, w, _, _ = gen.make_config(name, m=m, with_lora=False)
+        xd = to_dev(x)
+        vals, idx, scale = rtl.sparsify_2of4(xd)
+        y = rtl.sparse_linear_compressed(vals, idx, scale, to_dev(w))
+        torch.cuda.synchronize()
+        assert_y_close(y_to_f64(y), oracle.sparse_linear_ref(x, w), f"unfused {name}")
+
+
+def test_compressed_linear_full_headline_sampled():
+    cfg = gen.config("mlp_up")
+    say(f"[parity] compressed full mlp_up: M={cfg.m} K={cfg.k} N={cfg.n}")
+    x, w, _, _ = gen.make_config("mlp_up", with_lora=False)
+    vals, idx, scale = rtl.sparsify_2of4(to_dev(x))
+    y = rtl.sparse_linear_compressed(vals, idx, scale, to_dev(w))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(8), cfg.m - 1 - np.arange(8),
+                                     np.random.default_rng(cfg.seed + 100).choice(cfg.m, 48, replace=False)]))
+    ys = y_to_f64(y[torch.from_numpy(rows).to(DEV)])
+    assert_y_close(ys, oracle.sparse_linear_ref(x[rows], w), "compressed full mlp_up (sampled rows)")

@@ -195,6 +195,32 @@ def test_gather_form_equals_masked_dense_form():
     np.testing.assert_allclose(y1, y2, rtol=1e-12, atol=1e-12 * np.abs(y1).max())
 
 
+def test_compressed_linear_handworked():
+    """One group: kept values 2 and 3 at channels 1 and 3 (code 1 | 3 << 2),
+    scale 1.5, W row (1, 10, 100, 1000): y = 1.5 (2 * 10 + 3 * 1000) = 4530;
+    a second token with the pair at channels 0, 2 and no scale factor."""
+    vals = gen.f32_to_bf16_bits(np.array([[2.0, 3.0], [5.0, -1.0]], dtype=np.float32))
+    idx = np.array([[1 | (3 << 2)], [0 | (2 << 2)]], dtype=np.uint8)
+    w = gen.f32_to_bf16_bits(np.array([[1.0, 10.0, 100.0, 1000.0]], dtype=np.float32))
+    y = oracle.compressed_linear_ref(vals, idx, np.array([1.5, 1.0]), w, 4)
+    assert y.tolist() == [[4530.0], [5.0 * 1.0 - 1.0 * 100.0]]
+    y0 = oracle.compressed_linear_ref(vals, idx, None, w, 4)
+    assert y0.tolist() == [[3020.0], [-95.0]]
+
+
+def test_compressed_linear_equals_layer_without_lora():
+    """Compressing X and multiplying the compressed form with its scale is
+    the layer without the LoRA branch (r = 0), by two independent routes."""
+    for name in ("tiny",):
+        x, w, _, _ = _inputs(name)
+        k = x.shape[1]
+        _, _, s, i0, i1 = oracle.sparsify(x)
+        vals, idx = oracle.compress(x, i0, i1)
+        y1 = oracle.compressed_linear_ref(vals, idx, s, w, k)
+        y2 = oracle.sparse_linear_gather_ref(x, w)
+        np.testing.assert_allclose(y1, y2, rtol=1e-12, atol=1e-12 * np.abs(y2).max())
+
+
 def _exact_lora_factors(rng, n, k, r):
     a = gen.f32_to_bf16_bits(rng.integers(-1, 2, size=(r, k)).astype(np.float32) * 0.125)
     b = gen.f32_to_bf16_bits(rng.integers(-1, 2, size=(n, r)).astype(np.float32) * 0.125)
