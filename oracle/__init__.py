@@ -27,4 +27,8 @@ from .rtlynx_ref import (  # noqa: F401
     sparse_linear_gather_ref,
     lora_down_ref,
     compressed_linear_ref,
+    round_to_bf16,
+    group_compensation_scale,
+    sparsify_variant,
+    sparse_linear_variant_ref,
 )

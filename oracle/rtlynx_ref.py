@@ -270,3 +270,88 @@ def compressed_linear_ref(vals, idx, scale, w_bits, k: int) -> np.ndarray:
     if scale is not None:
         y = y * np.asarray(scale, dtype=np.float64)[:, None]
     return y
+
+
+# ---------------------------------------------------------------------------
+# Compensation and LoRA-input variants the pages leave open (each reading is
+# listed with the default one in the design doc).  The default of every function
+# above is comp="token", lora="residual".
+
+def round_to_bf16(v) -> np.ndarray:
+    """fp64 -> nearest bf16 value (8 significant bits), ties to even, exact:
+    v = f 2^e with 0.5 <= |f| < 1, f is rounded to a multiple of 2^-8.  For
+    the normal bf16 range (|v| >= 2^-126), which all values here are in."""
+    v = np.asarray(v, dtype=np.float64)
+    f, e = np.frexp(v)
+    return np.ldexp(np.rint(f * 256.0) / 256.0, e)
+
+
+def group_compensation_scale(x: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Per group of 4: (L1 of the group) / (L1 of its kept pair), 1 where the
+    kept pair is zero (then the whole group is).  [M, K/4]."""
+    m, k = x.shape
+    ax = np.abs(x).reshape(m, k // 4, 4)
+    mk = mask.reshape(m, k // 4, 4)
+    lk = np.where(mk, ax, 0.0).sum(axis=2)
+    tot = ax.sum(axis=2)
+    out = np.ones_like(lk)
+    nz = lk > 0
+    out[nz] = tot[nz] / lk[nz]
+    return out
+
+
+def sparsify_variant(bits, comp: str = "token"):
+    """S(X) under a compensation variant (ai-feeds summary, 核心模块 1 leaves
+    the granularity open):
+
+    * "token":  s per token (the default, = ``sparsify``);
+    * "none":   no compensation, S(X) = M * X;
+    * "tensor": one s for the whole X, (sum of all L1) / (sum of kept L1);
+    * "group":  s per group of 4, applied to the kept pair and rounded to
+                bf16 (a factor that varies along K can only live in the
+                compressed operand itself).
+
+    Returns (S [M, K] fp64, mask)."""
+    x = bf16_bits_to_f64(bits)
+    mask, _, _ = select_2of4(bits)
+    kept = np.where(mask, x, 0.0)
+    if comp == "token":
+        lk, lp = l1_stats(x, mask)
+        return kept * compensation_scale(lk, lp)[:, None], mask
+    if comp == "none":
+        return kept, mask
+    if comp == "tensor":
+        lk, lp = l1_stats(x, mask)
+        lk_t, lp_t = lk.sum(), lp.sum()
+        s = (lk_t + lp_t) / lk_t if lk_t > 0 else 1.0
+        return kept * s, mask
+    if comp == "group":
+        sg = group_compensation_scale(x, mask)
+        return round_to_bf16(kept * np.repeat(sg, 4, axis=1)), mask
+    raise ValueError(comp)
+
+
+def sparse_linear_variant_ref(x_bits, w_bits, a_bits=None, b_bits=None, alpha: float = 1.0,
+                              comp: str = "token", lora: str = "residual"):
+    """Y = S(X) W^T + alpha (R A^T) B^T in fp64 with S from
+    ``sparsify_variant(comp)`` and the LoRA input R (qingkeai article, 03.2,
+    says the branch restores the pruned information; which tensor carries it
+    is open):
+
+    * "residual": R = X - S(X) (the default);
+    * "pruned":   R = (1 - M) * X, the pruned values only;
+    * "input":    R = X, a plain LoRA beside the sparse product."""
+    x = bf16_bits_to_f64(x_bits)
+    sx, mask = sparsify_variant(x_bits, comp)
+    y = sx @ bf16_bits_to_f64(w_bits).T
+    if a_bits is not None and b_bits is not None and np.asarray(a_bits).shape[0] > 0:
+        if lora == "residual":
+            rin = x - sx
+        elif lora == "pruned":
+            rin = np.where(mask, 0.0, x)
+        elif lora == "input":
+            rin = x
+        else:
+            raise ValueError(lora)
+        y = y + alpha * ((rin @ bf16_bits_to_f64(a_bits).T) @ bf16_bits_to_f64(b_bits).T)
+    return y

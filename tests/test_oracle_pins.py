@@ -373,3 +373,85 @@ def test_unmutated_oracle_passes_pin_subset():
                                       _lora_on_pruned_only, _lora_sign_flip, _keep_smallest])
 def test_planted_mistake_is_caught(mutation):
     assert not _pins_pass(_mutant(mutation))
+
+
+# ---------------------------------------------------------------------------
+# Compensation and LoRA-input variants.
+
+def test_round_to_bf16_handworked_and_nearest():
+    r = oracle.round_to_bf16
+    assert r(1.0 + 2.0 ** -8) == 1.0                    # tie: to even
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6    # tie: to even (upwards)
+    assert r(1.0 + 3 * 2.0 ** -9) == 1.0 + 2.0 ** -7
+    assert r(-3.0) == -3.0 and r(0.0) == 0.0
+    assert r(0.1) == 0.10009765625
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal(2000) * 10.0 ** rng.integers(-6, 6, 2000)
+    q = r(v)
+    # a bf16 value: the fp32 pattern has zero low half ...
+    assert (np.float32(q).view(np.uint32) & 0xFFFF == 0).all()
+    # ... and no bf16 neighbour is closer
+    bits = np.float32(q).view(np.uint32) >> 16
+    for d in (-1, 1):
+        nb = ((bits.astype(np.int64) + d).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert (np.abs(q - v) <= np.abs(nb - v)).all()
+
+
+def test_variant_default_is_the_layer():
+    x, w, a, b = _inputs("tiny")
+    np.testing.assert_allclose(oracle.sparse_linear_variant_ref(x, w, a, b, 0.7),
+                               oracle.sparse_linear_ref(x, w, a, b, 0.7), rtol=1e-13, atol=1e-13)
+
+
+def test_variant_none_pruned_recovers_dense_when_w_equals_ba():
+    """No compensation and the pruned values as the LoRA input: with W = B A
+    exactly, (M*X) W^T + ((1-M)*X) A^T B^T = X W^T."""
+    rng = np.random.default_rng(21)
+    w, a, b = _exact_lora_factors(rng, 24, 64, 8)
+    x = gen.mixture_bernoulli(rng, 12, 64)
+    y = oracle.sparse_linear_variant_ref(x, w, a, b, 1.0, comp="none", lora="pruned")
+    np.testing.assert_allclose(y, oracle.dense_linear_ref(x, w), rtol=1e-12, atol=1e-12)
+
+
+def test_variant_input_lora_with_zero_weight_is_plain_lora():
+    rng = np.random.default_rng(22)
+    x = gen.mixture_bernoulli(rng, 9, 32)
+    a = gen.gaussian_bits(rng, (4, 32), 0.1)
+    b = gen.gaussian_bits(rng, (5, 4), 0.1)
+    w = np.zeros((5, 32), dtype=np.uint16)
+    f = oracle.bf16_bits_to_f64
+    for comp in ("token", "none", "tensor", "group"):
+        y = oracle.sparse_linear_variant_ref(x, w, a, b, 0.5, comp=comp, lora="input")
+        np.testing.assert_allclose(y, 0.5 * (f(x) @ f(a).T) @ f(b).T, rtol=1e-12, atol=1e-15)
+
+
+def test_variant_tensor_scale_restores_the_tensor_l1():
+    rng = np.random.default_rng(23)
+    x = gen.mixture_bernoulli(rng, 10, 64)
+    sx, mask = oracle.sparsify_variant(x, "tensor")
+    xf = oracle.bf16_bits_to_f64(x)
+    np.testing.assert_allclose(np.abs(sx).sum(), np.abs(xf).sum(), rtol=1e-13)
+    # one token, or identical tokens: the tensor factor is the token factor
+    for xx in (x[:1], np.repeat(x[:1], 5, axis=0)):
+        np.testing.assert_allclose(oracle.sparsify_variant(xx, "tensor")[0],
+                                   oracle.sparsify_variant(xx, "token")[0], rtol=1e-14)
+    # the none variant keeps the values
+    sn, mn = oracle.sparsify_variant(x, "none")
+    assert np.array_equal(sn, np.where(mn, xf, 0.0))
+
+
+def test_variant_group_scale_restores_each_group_within_rounding():
+    rng = np.random.default_rng(24)
+    x = gen.mixture_bernoulli(rng, 16, 128)
+    sx, mask = oracle.sparsify_variant(x, "group")
+    xf = oracle.bf16_bits_to_f64(x)
+    g_s = np.abs(sx).reshape(16, 32, 4).sum(axis=2)
+    g_x = np.abs(xf).reshape(16, 32, 4).sum(axis=2)
+    # each kept value is s_g x rounded to bf16: within 2^-9 relative each
+    assert (np.abs(g_s - g_x) <= 2.0 ** -8 * g_x + 1e-300).all()
+    # values are bf16 and kept positions only
+    assert (np.float32(sx).view(np.uint32) & 0xFFFF == 0).all()
+    assert (sx[~mask] == 0).all()
+    # at most two non-zeros per group: S(X) = X exactly
+    x2 = gen.at_most_two_nonzero(rng, 8, 64)
+    assert np.array_equal(oracle.sparsify_variant(x2, "group")[0], oracle.bf16_bits_to_f64(x2))
