@@ -25,6 +25,7 @@ __all__ = [
     "RtlError", "lib", "library_path", "sparsify_2of4", "sparse_linear", "dense_linear",
     "sparse_linear_workspace_bytes", "version", "status_string", "STATUS", "prepare", "apply", "Prepared",
     "FOLD_SCALE", "MAX_LORA_RANK", "sparse_linear_compressed",
+    "COMP_TOKEN", "COMP_NONE", "COMP_TENSOR", "COMP_GROUP", "LORA_RESIDUAL", "LORA_PRUNED", "LORA_INPUT",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +38,10 @@ STATUS = {
 }
 FOLD_SCALE = 0x1
 MAX_LORA_RANK = 128
+# Variants of the layer (rtl_sparse_linear_prepare_variant): compensation ...
+COMP_TOKEN, COMP_NONE, COMP_TENSOR, COMP_GROUP = 0x0, 0x1, 0x2, 0x3
+# ... | LoRA input.
+LORA_RESIDUAL, LORA_PRUNED, LORA_INPUT = 0x0, 0x4, 0x8
 
 _c_i64, _c_u32, _c_vp, _c_f = ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
 
@@ -49,6 +54,8 @@ _SIGNATURES = {
                                                  ctypes.c_size_t, _c_vp]),
     "rtl_sparse_linear_apply": (ctypes.c_int, [_c_vp, ctypes.c_size_t, _c_vp, _c_vp, _c_i64, _c_i64,
                                                _c_i64, _c_i64, _c_vp, _c_vp]),
+    "rtl_sparse_linear_prepare_variant": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, ctypes.c_float,
+                                                         _c_u32, _c_vp, ctypes.c_size_t, _c_vp]),
     "rtl_sparse_linear_compressed": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                                                     _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "rtl_dense_linear": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
@@ -177,8 +184,10 @@ class Prepared:
         self.workspace, self.m, self.k, self.r, self.lead_shape = workspace, m, k, r, lead_shape
 
 
-def prepare(x, lora_a=None, lora_scale: float = 1.0, workspace=None) -> Prepared:
-    """First half of sparse_linear: reads x once (rtl_sparse_linear_prepare)."""
+def prepare(x, lora_a=None, lora_scale: float = 1.0, workspace=None, variant: int = 0) -> Prepared:
+    """First half of sparse_linear: reads x once (rtl_sparse_linear_prepare,
+    or rtl_sparse_linear_prepare_variant for a nonzero ``variant``: one of
+    COMP_* | one of LORA_*)."""
     torch = _torch()
     x2 = _as_2d(x, "x")
     m, k = x2.shape
@@ -191,9 +200,15 @@ def prepare(x, lora_a=None, lora_scale: float = 1.0, workspace=None) -> Prepared
     need = sparse_linear_workspace_bytes(m, k, r)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
-    st = lib().rtl_sparse_linear_prepare(x2.data_ptr(), lora_a.data_ptr() if r else None, m, k, r,
-                                         float(lora_scale), workspace.data_ptr(), workspace.numel(), _stream())
-    _check(st, "rtl_sparse_linear_prepare")
+    if variant:
+        st = lib().rtl_sparse_linear_prepare_variant(x2.data_ptr(), lora_a.data_ptr() if r else None, m, k, r,
+                                                     float(lora_scale), int(variant), workspace.data_ptr(),
+                                                     workspace.numel(), _stream())
+        _check(st, "rtl_sparse_linear_prepare_variant")
+    else:
+        st = lib().rtl_sparse_linear_prepare(x2.data_ptr(), lora_a.data_ptr() if r else None, m, k, r,
+                                             float(lora_scale), workspace.data_ptr(), workspace.numel(), _stream())
+        _check(st, "rtl_sparse_linear_prepare")
     return Prepared(workspace, m, k, r, tuple(x.shape[:-1]))
 
 

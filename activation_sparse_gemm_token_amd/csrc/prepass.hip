@@ -44,7 +44,8 @@ struct Quad {
   uint32_t kcode, pcode;
 };
 
-__device__ __forceinline__ void select_quad(const uint32_t (&w)[8], Quad& q, float& lk, float& lp) {
+__device__ __forceinline__ void select_quad(const uint32_t (&w)[8], Quad& q, float& lk, float& lp,
+                                            bool fold = false, u32x4* kept_f = nullptr) {
   q.kcode = 0;
   q.pcode = 0;
 #pragma unroll
@@ -59,14 +60,17 @@ __device__ __forceinline__ void select_quad(const uint32_t (&w)[8], Quad& q, flo
     q.pcode |= code_from_selector(ps) << (4 * g);
     lk = add_mag_pair(lk, r.first, r.second);
     lp = add_mag_pair(lp, r.third, r.fourth);
+    if (fold) (*kept_f)[g] = fold_group(q.kept[g], r);
   }
 }
 
 // The kept half only (the pre-pass with DMA-streamed operands forms the
 // LoRA-down from the whole input words instead of the pruned half): kept
-// operand words and their 16-bit index field; both L1 sums as above.
+// operand words and their 16-bit index field; both L1 sums as above; with
+// FOLD also the kept words scaled per group (fold_group).
+template <bool FOLD>
 __device__ __forceinline__ void select_quad_kept(const uint32_t (&w)[8], u32x4& kept, uint32_t& kcode,
-                                                 float& lk, float& lp) {
+                                                 float& lk, float& lp, u32x4& kept_f) {
   kcode = 0;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -77,6 +81,7 @@ __device__ __forceinline__ void select_quad_kept(const uint32_t (&w)[8], u32x4& 
     kcode |= code_from_selector(ks) << (4 * g);
     lk = add_mag_pair(lk, r.first, r.second);
     lp = add_mag_pair(lp, r.third, r.fourth);
+    if constexpr (FOLD) kept_f[g] = fold_group(kept[g], r);
   }
 }
 
@@ -131,12 +136,12 @@ __device__ __forceinline__ bf16x16 load_b_sparse(__amdgpu_buffer_rsrc_t br, int6
   return __builtin_bit_cast(bf16x16, v);
 }
 
-template <bool ALIGNED16, int NCB>
+template <bool ALIGNED16, int NCB, bool FOLD>
 __global__ void __launch_bounds__(64 * kWaves)
 prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora_a,
                int64_t M, int64_t K, int64_t r, float alpha,
                u32x4* __restrict__ xv, uint16_t* __restrict__ xi, float* __restrict__ s_out,
-               u32x4* __restrict__ t_out, int64_t kpairs, int64_t rsteps) {
+               u32x4* __restrict__ t_out, int64_t kpairs, int64_t rsteps, int comp, int lora) {
   // NCB = 16-wide column blocks of the LoRA rank covered (0: no LoRA branch).
   constexpr int NT = NCB > 0 ? NCB : 1;
   __shared__ float red_l[kWaves][2][16];
@@ -200,11 +205,13 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
     __builtin_amdgcn_sched_barrier(0);
     const int64_t ks0 = 2 * p;
     Quad q0, q1;
-    select_quad(x0, q0, lk, lp);
-    select_quad(x1, q1, lk, lp);
+    constexpr bool fold = FOLD;        // per-group compensation (comp == kCompGroup)
+    u32x4 f0 = (u32x4){0, 0, 0, 0}, f1 = (u32x4){0, 0, 0, 0};
+    select_quad(x0, q0, lk, lp, fold, &f0);
+    select_quad(x1, q1, lk, lp, fold, &f1);
     const int64_t grp = mb >> 3, sub = mb & 7;
-    xv[((grp * ksteps + ks0) * 8 + sub) * 64 + lane] = q0.kept;
-    xv[((grp * ksteps + ks0 + 1) * 8 + sub) * 64 + lane] = q1.kept;
+    xv[((grp * ksteps + ks0) * 8 + sub) * 64 + lane] = fold ? f0 : q0.kept;
+    xv[((grp * ksteps + ks0 + 1) * 8 + sub) * 64 + lane] = fold ? f1 : q1.kept;
     xi[((grp * ksteps + ks0) * 64 + lane) * 8 + sub] = (uint16_t)q0.kcode;
     xi[((grp * ksteps + ks0 + 1) * 64 + lane) * 8 + sub] = (uint16_t)q1.kcode;
     if constexpr (NCB > 0) {
@@ -214,6 +221,15 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
         tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.pruned), b[c][0], tp[c], (int)q0.pcode, 0, 0);
         tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.kept), b[c][1], tk[c], (int)q1.kcode, 0, 0);
         tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.pruned), b[c][1], tp[c], (int)q1.pcode, 0, 0);
+      }
+      if (fold && lora == kLoraResidual) {
+        // R's kept part is M*X - S(X): the folded words with their sign
+        // flipped (exact) join tk.
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) {
+          tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, f0 ^ 0x80008000u), b[c][0], tk[c], (int)q0.kcode, 0, 0);
+          tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, f1 ^ 0x80008000u), b[c][1], tk[c], (int)q1.kcode, 0, 0);
+        }
       }
     }
   }
@@ -230,21 +246,28 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
     float a = 0.f, b = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) { a += red_l[w][0][threadIdx.x]; b += red_l[w][1][threadIdx.x]; }
-    const float s = a > 0.f ? (a + b) / a : 1.0f;
+    // Per token, or 1 (none; per group: in the operand), or the whole
+    // activation's factor, which the statistics pass left in s_out.
+    const float s = comp == kCompToken ? (a > 0.f ? (a + b) / a : 1.0f)
+                  : comp == kCompTensor ? s_out[mb * 16 + threadIdx.x] : 1.0f;
     s_sh[threadIdx.x] = s;
     s_out[mb * 16 + threadIdx.x] = s;
   }
   if constexpr (NCB > 0) {
     __syncthreads();
     // Accumulator layout of a 16x16 block: lane l holds column l % 16 of rows
-    // 4 (l / 16) + i.  T_w = T_pruned + (1 - s) T_kept per wavefront, then
-    // summed over wavefronts in a fixed order.
+    // 4 (l / 16) + i.  T_w = T_pruned + c T_kept per wavefront, then summed
+    // over wavefronts in a fixed order: c = 1 - s for the residual (for
+    // per-group folding T_kept already holds (M*X - S(X)) A^T: c = 1), 0
+    // for the pruned values, 1 for the whole input.
+    constexpr bool folded = FOLD;
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 4 * (lane >> 4) + i;
-        red_t[wave][rr][c * 16 + (lane & 15)] = tp[c][i] + (1.0f - s_sh[rr]) * tk[c][i];
+        const float ck = lora == kLoraResidual ? (folded ? 1.0f : 1.0f - s_sh[rr]) : lora == kLoraPruned ? 0.0f : 1.0f;
+        red_t[wave][rr][c * 16 + (lane & 15)] = tp[c][i] + ck * tk[c][i];
       }
     }
     __syncthreads();
@@ -411,12 +434,16 @@ __device__ __forceinline__ uint32_t swz(int n, int c) { return (uint32_t)(n * 12
 // FULLK (K % 128 == 0, every k-step inside K): the copy and store offsets
 // are computed once and advanced by a scalar offset per step; otherwise
 // they are recomputed per step with the channel-tail guards.
-template <int NCB, bool FULLK>
+//
+// FOLD (per-group compensation): the stored operand is the kept words scaled
+// per group and rounded (fold_group); the LoRA-down subtracts the product of
+// that operand.  comp and lora select the other variants at run time.
+template <int NCB, bool FULLK, bool FOLD>
 __global__ void __launch_bounds__(64 * kDWaves, 1)
 prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora_a,
                    int64_t M, int64_t K, int64_t r, float alpha,
                    u32x4* __restrict__ xv, uint16_t* __restrict__ xi, float* __restrict__ s_out,
-                   u32x4* __restrict__ t_out, int64_t ksteps, int64_t rsteps) {
+                   u32x4* __restrict__ t_out, int64_t ksteps, int64_t rsteps, int comp, int lora) {
   static_assert(NCB == 2 || NCB == 4, "ranks 32 or 64");
   constexpr int kXBytes = 2048;                       // 16 tokens x 128 B
   constexpr int kABytes = NCB * 2048;                 // 16 NCB ranks x 128 B
@@ -542,11 +569,18 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
       const u32x4 d0 = *reinterpret_cast<const u32x4*>(xs + xd0);
       const u32x4 d1 = *reinterpret_cast<const u32x4*>(xs + xd1);
       const uint32_t w[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-      u32x4 kept;
+      u32x4 kept, kept_f;
       uint32_t kcode;
-      select_quad_kept(w, kept, kcode, lk, lp);
+      select_quad_kept<FOLD>(w, kept, kcode, lk, lp, kept_f);
       const uint32_t so_v = __builtin_amdgcn_readfirstlane(8192u * (uint32_t)t);
       const uint32_t so_i = __builtin_amdgcn_readfirstlane(1024u * (uint32_t)t);
+      // The LoRA-down's kept operand: the stored (folded) words for the
+      // residual, the input words otherwise.
+      u32x4 kept_l = kept;
+      if constexpr (FOLD) {
+        if (lora == kLoraResidual) kept_l = kept_f;
+        kept = kept_f;
+      }
       __builtin_amdgcn_raw_buffer_store_b128(kept, vr, sv0, so_v, 0);
       __builtin_amdgcn_raw_buffer_store_b16((uint16_t)kcode, ir, si0, so_i, 0);
       const char* as = ring + kXStages * kXBytes + (t % kAStages) * kABytes;
@@ -555,7 +589,7 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(as + c * 2048 + bo0);
         const u32x4 b1 = *reinterpret_cast<const u32x4*>(as + c * 2048 + bo1);
         const bf16x16 bf = __builtin_bit_cast(bf16x16, (u32x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]});
-        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, kept), bf, tk[c], (int)kcode, 0, 0);
+        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, kept_l), bf, tk[c], (int)kcode, 0, 0);
         tx[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, d0), __builtin_bit_cast(bf16x8, b0), tx[c], 0, 0, 0);
         tx[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, d1), __builtin_bit_cast(bf16x8, b1), tx[c], 0, 0, 0);
       }
@@ -578,20 +612,26 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     float a = 0.f, b = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < kDWaves; ++w2) { a += red.l[w2][0][threadIdx.x]; b += red.l[w2][1][threadIdx.x]; }
-    const float sc = a > 0.f ? (a + b) / a : 1.0f;
+    // Per token, or 1 (none; per group: in the operand), or the whole
+    // activation's factor, which the statistics pass left in s_out.
+    const float sc = comp == kCompToken ? (a > 0.f ? (a + b) / a : 1.0f)
+                   : comp == kCompTensor ? s_out[mb * 16 + threadIdx.x] : 1.0f;
     red.s[threadIdx.x] = sc;
     s_out[mb * 16 + threadIdx.x] = sc;
   }
   __syncthreads();
   // Accumulator layout of a 16x16 block: lane l holds column l % 16 of rows
-  // 4 (l / 16) + i.  T_w = (X A^T)_w - s (M*X A^T)_w per wavefront, then
-  // summed over wavefronts in a fixed order.
+  // 4 (l / 16) + i.  T_w = (X A^T)_w - c (kept A^T)_w per wavefront, then
+  // summed over wavefronts in a fixed order: c = s for the residual (the
+  // kept operand already folded for per-group compensation, where s = 1),
+  // 1 for the pruned values, 0 for the whole input.
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = 4 * (lane >> 4) + i;
-      red.t[wave][rr][c * 16 + (lane & 15)] = tx[c][i] - red.s[rr] * tk[c][i];
+      const float cx = lora == kLoraResidual ? red.s[rr] : lora == kLoraPruned ? 1.0f : 0.0f;
+      red.t[wave][rr][c * 16 + (lane & 15)] = tx[c][i] - cx * tk[c][i];
     }
   }
   __syncthreads();
@@ -621,9 +661,72 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-tensor compensation: one factor for the whole activation,
+// (sum of all L1) / (sum of kept L1).  Two passes before the pre-pass:
+// l1_rows_kernel writes each token's kept and pruned L1 (the selection of
+// the pre-pass, one wavefront per token, fixed-order lane reduction);
+// tensor_scale_kernel (one workgroup) adds them in a fixed order in fp64 and
+// writes the factor into every entry of the scale region, where the
+// pre-pass reads it for its tokens.
+
+template <bool A16>
+__global__ void __launch_bounds__(256)
+l1_rows_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, float* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, M * K * 2);
+  float lk = 0.f, lp = 0.f;
+  // 16 channels (4 groups) per lane and iteration, guarded by K.
+  for (int64_t k = 16 * lane; k < K; k += 16 * 64) {
+    uint32_t w[8];
+    load_quad<A16>(xr, row, true, k, K, w);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const Group4 r = rank_group(w[2 * g], w[2 * g + 1]);
+      lk = add_mag_pair(lk, r.first, r.second);
+      lp = add_mag_pair(lp, r.third, r.fourth);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lk += __shfl_xor(lk, o, 64);
+    lp += __shfl_xor(lp, o, 64);
+  }
+  if (lane == 0) {
+    part[2 * row] = lk;
+    part[2 * row + 1] = lp;
+  }
+}
+
+__global__ void __launch_bounds__(1024)
+tensor_scale_kernel(const float* __restrict__ part, int64_t M, float* __restrict__ s, int64_t mp) {
+  __shared__ double red[2][1024];
+  double a = 0.0, b = 0.0;
+  for (int64_t i = threadIdx.x; i < M; i += 1024) {
+    a += (double)part[2 * i];
+    b += (double)part[2 * i + 1];
+  }
+  red[0][threadIdx.x] = a;
+  red[1][threadIdx.x] = b;
+  __syncthreads();
+  for (int h = 512; h >= 1; h >>= 1) {
+    if ((int)threadIdx.x < h) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + h];
+      red[1][threadIdx.x] += red[1][threadIdx.x + h];
+    }
+    __syncthreads();
+  }
+  const double lk = red[0][0], lp = red[1][0];
+  const float st = lk > 0.0 ? (float)((lk + lp) / lk) : 1.0f;
+  for (int64_t i = threadIdx.x; i < mp; i += 1024) s[i] = st;
+}
+
 template <bool A16>
 hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M, int64_t K,
-                            int64_t r, float alpha, const WsLayout& L, char* ws, hipStream_t stream) {
+                            int64_t r, float alpha, int comp, int lora, const WsLayout& L, char* ws,
+                            hipStream_t stream) {
   // 8 workgroups per group of 8 16-token blocks, groups rounded up to a
   // multiple of 8 (the kernel's XCD-grouped mapping).
   const int64_t ngroups = L.mp / 128;
@@ -634,42 +737,56 @@ hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M
   u32x4* t = reinterpret_cast<u32x4*>(ws + L.off_t);
   const int64_t kpairs = L.kp / 128, rsteps = L.rp / 32;
   const int ncb = (int)(L.rp / 16);
+  if (comp == kCompTensor) {
+    // Per-token L1 pairs go to the operand region (2 M floats <= its
+    // mp kp bytes), which the pre-pass overwrites afterwards.
+    float* part = reinterpret_cast<float*>(ws + L.off_xv);
+    l1_rows_kernel<A16><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream>>>(x, M, K, part);
+    tensor_scale_kernel<<<dim3(1), dim3(1024), 0, stream>>>(part, M, s, L.mp);
+  }
   if constexpr (A16) {
     // r <= 64: the DMA-streamed pre-pass, one workgroup of 4 wavefronts per
     // 16-token block (same grid and mapping).
     const dim3 dblock(64 * kDWaves);
     const int64_t ksteps = L.kp / 64;
     const bool full = K % 128 == 0;
-    if (r > 0 && ncb <= 2) {
-      if (full) prepass_dma_kernel<2, true><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
-      else prepass_dma_kernel<2, false><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
-      return hipGetLastError();
-    }
+    const bool fold = comp == kCompGroup;
+#define RTL_DMA_PREPASS(NCB_, FULL_, FOLD_)                                                              \
+  prepass_dma_kernel<NCB_, FULL_, FOLD_><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, \
+                                                                      ksteps, rsteps, comp, lora)
     if (r > 0 && ncb <= 4) {
-      if (full) prepass_dma_kernel<4, true><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
-      else prepass_dma_kernel<4, false><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, ksteps, rsteps);
+      if (ncb <= 2) {
+        if (full) { if (fold) RTL_DMA_PREPASS(2, true, true); else RTL_DMA_PREPASS(2, true, false); }
+        else { if (fold) RTL_DMA_PREPASS(2, false, true); else RTL_DMA_PREPASS(2, false, false); }
+      } else {
+        if (full) { if (fold) RTL_DMA_PREPASS(4, true, true); else RTL_DMA_PREPASS(4, true, false); }
+        else { if (fold) RTL_DMA_PREPASS(4, false, true); else RTL_DMA_PREPASS(4, false, false); }
+      }
+#undef RTL_DMA_PREPASS
       return hipGetLastError();
     }
   }
-  if (r == 0)
-    prepass_kernel<A16, 0><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, 0);
-  else if (ncb <= 2)
-    prepass_kernel<A16, 2><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, rsteps);
-  else if (ncb <= 4)
-    prepass_kernel<A16, 4><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, rsteps);
-  else
-    prepass_kernel<A16, 8><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, rsteps);
+#define RTL_PREPASS(NCB_, FOLD_, RS_)                                                                  \
+  prepass_kernel<A16, NCB_, FOLD_><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, \
+                                                               RS_, comp, lora)
+  const bool fold = comp == kCompGroup;
+  if (r == 0) { if (fold) RTL_PREPASS(0, true, 0); else RTL_PREPASS(0, false, 0); }
+  else if (ncb <= 2) { if (fold) RTL_PREPASS(2, true, rsteps); else RTL_PREPASS(2, false, rsteps); }
+  else if (ncb <= 4) { if (fold) RTL_PREPASS(4, true, rsteps); else RTL_PREPASS(4, false, rsteps); }
+  else { if (fold) RTL_PREPASS(8, true, rsteps); else RTL_PREPASS(8, false, rsteps); }
+#undef RTL_PREPASS
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prepass(const uint16_t* x, const uint16_t* lora_a, int64_t M, int64_t K,
-                          int64_t r, float lora_scale, void* workspace, hipStream_t stream) {
+                          int64_t r, float lora_scale, void* workspace, hipStream_t stream, int comp,
+                          int lora) {
   const WsLayout L = ws_layout(M, K, r);
   char* ws = static_cast<char*>(workspace);
-  if (K % 8 == 0) return launch_prepass_t<true>(x, lora_a, M, K, r, lora_scale, L, ws, stream);
-  return launch_prepass_t<false>(x, lora_a, M, K, r, lora_scale, L, ws, stream);
+  if (K % 8 == 0) return launch_prepass_t<true>(x, lora_a, M, K, r, lora_scale, comp, lora, L, ws, stream);
+  return launch_prepass_t<false>(x, lora_a, M, K, r, lora_scale, comp, lora, L, ws, stream);
 }
 
 }  // namespace rtl

@@ -124,6 +124,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// Variants of the layer that the pages leave open (rtl_sparse_linear_prepare_variant).
+// Compensation: per token (default), none, one factor for the whole
+// activation, or per group of 4 folded into the kept values.
+constexpr int kCompToken = 0, kCompNone = 1, kCompTensor = 2, kCompGroup = 3;
+// LoRA input: the pruned residual X - S(X) (default), the pruned values
+// (1 - M) * X, or the whole input X.
+constexpr int kLoraResidual = 0, kLoraPruned = 1, kLoraInput = 2;
+
+// The kept pair of one group (operand word, channel order) scaled by the
+// group's compensation factor -- L1 of the group over L1 of the kept pair,
+// 1 for a zero pair -- and rounded to bf16.
+__device__ __forceinline__ uint32_t fold_group(uint32_t kept_word, const Group4& g) {
+  const float lkg = add_mag_pair(0.f, g.first, g.second);
+  const float lpg = add_mag_pair(0.f, g.third, g.fourth);
+  const float sg = lkg > 0.f ? (lkg + lpg) / lkg : 1.0f;
+  return pack_bf16x2(bf16_lo_to_f32(kept_word) * sg, bf16_hi_to_f32(kept_word) * sg);
+}
+
 // Buffer resource over a whole tensor (raw, stride 0): loads past `bytes`
 // return zeros instead of faulting, stores there are dropped.  The host
 // keeps every tensor below 2 GiB, so sizes and offsets fit 32 bits.  Guarded

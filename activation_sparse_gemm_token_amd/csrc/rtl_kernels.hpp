@@ -13,7 +13,8 @@ hipError_t launch_sparsify_2of4(const uint16_t* x, int64_t M, int64_t K, uint16_
 // Pre-pass of the fused path: selection, compression into the structured-
 // sparse matrix-core operand order, per-token scale, LoRA-down product.
 hipError_t launch_prepass(const uint16_t* x, const uint16_t* lora_a, int64_t M, int64_t K,
-                          int64_t r, float lora_scale, void* workspace, hipStream_t stream);
+                          int64_t r, float lora_scale, void* workspace, hipStream_t stream,
+                          int comp = 0, int lora = 0);
 
 // Sparse GEMM on the compressed operand plus the scale and LoRA-up epilogue.
 // `compute_units`: the device's CU count (the persistent grid's size).

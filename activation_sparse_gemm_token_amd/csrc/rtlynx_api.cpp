@@ -121,6 +121,25 @@ RTL_API rtl_status rtl_sparse_linear_prepare(const uint16_t* x, const uint16_t* 
                                       static_cast<hipStream_t>(hip_stream)));
 }
 
+RTL_API rtl_status rtl_sparse_linear_prepare_variant(const uint16_t* x, const uint16_t* lora_a, int64_t M,
+                                                     int64_t K, int64_t r, float lora_scale, uint32_t variant,
+                                                     void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const uint32_t comp = variant & 3u, lora = (variant >> 2) & 3u;
+  if ((variant & ~0xFu) != 0 || lora == 3u) return RTL_ERR_BAD_FLAGS;
+  if (!dims_ok(M, K) || r < 0 || r > RTL_MAX_LORA_RANK) return RTL_ERR_BAD_SHAPE;
+  if (!layer_sizes_ok(M, 0, K, r)) return RTL_ERR_BAD_SHAPE;
+  if (M == 0) return RTL_OK;
+  if (x == nullptr) return RTL_ERR_NULL_POINTER;
+  if (r > 0 && lora_a == nullptr) return RTL_ERR_NULL_POINTER;
+  if (!aligned16(x) || (r > 0 && !aligned16(lora_a))) return RTL_ERR_MISALIGNED;
+  if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
+  const rtl_status d = check_device();
+  if (d != RTL_OK) return d;
+  return from_hip(rtl::launch_prepass(x, r > 0 ? lora_a : nullptr, M, K, r, lora_scale, workspace,
+                                      static_cast<hipStream_t>(hip_stream), (int)comp, (int)lora));
+}
+
 RTL_API rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspace_bytes,
                                            const uint16_t* w, const uint16_t* lora_b, int64_t M,
                                            int64_t N, int64_t K, int64_t r, uint16_t* y,

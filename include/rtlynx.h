@@ -160,6 +160,52 @@ rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspace_bytes
                                    uint16_t* y, void* hip_stream);
 
 /*
+ * Variants of the layer the pages leave open (for rtl_sparse_linear_prepare_variant).
+ * Compensation -- how the pruned L1 mass returns to the kept values (ai-feeds
+ * summary, 核心模块 1, and qingkeai article, section 03.1, give the idea, not
+ * the granularity):
+ *   RTL_COMP_TOKEN   per token, s = (Lk + Lp) / Lk, applied to the fp32
+ *                    accumulators (the default; what rtl_sparse_linear does);
+ *   RTL_COMP_NONE    no compensation, s = 1;
+ *   RTL_COMP_TENSOR  one factor for the whole activation,
+ *                    (sum over tokens of Lk + Lp) / (sum of Lk), 1 if that is 0;
+ *   RTL_COMP_GROUP   per group of 4, (L1 of the group) / (L1 of its kept pair),
+ *                    multiplied into the kept values, which are then rounded to
+ *                    bf16 (a factor that varies along K can only live in the
+ *                    compressed operand); s = 1.
+ * LoRA input R of T = R A^T (qingkeai article, section 03.2: the branch
+ * restores the pruned information):
+ *   RTL_LORA_RESIDUAL  R = X - S(X) (the default);
+ *   RTL_LORA_PRUNED    R = (1 - M) * X, the pruned values;
+ *   RTL_LORA_INPUT     R = X.
+ * variant = one RTL_COMP_* | one RTL_LORA_*.
+ */
+#define RTL_COMP_TOKEN 0x0u
+#define RTL_COMP_NONE 0x1u
+#define RTL_COMP_TENSOR 0x2u
+#define RTL_COMP_GROUP 0x3u
+#define RTL_LORA_RESIDUAL 0x0u
+#define RTL_LORA_PRUNED 0x4u
+#define RTL_LORA_INPUT 0x8u
+
+/*
+ * rtl_sparse_linear_prepare_variant - rtl_sparse_linear_prepare for one of
+ * the variants above; rtl_sparse_linear_apply then completes the layer
+ *
+ *   y = bf16( S(X) W^T + lora_scale * (R A^T) B^T )
+ *
+ * with S and R as the variant defines them.  Arguments, workspace size and
+ * errors as for rtl_sparse_linear_prepare; an unknown bit in variant, or
+ * both RTL_LORA_* bits, gives RTL_ERR_BAD_FLAGS.  RTL_COMP_TENSOR runs two
+ * more kernels on the stream first (the activation's L1 statistics, read from
+ * x, and their fixed-order fp64 sum), so the result is deterministic.
+ */
+rtl_status rtl_sparse_linear_prepare_variant(const uint16_t* x, const uint16_t* lora_a,
+                                             int64_t M, int64_t K, int64_t r, float lora_scale,
+                                             uint32_t variant, void* workspace,
+                                             size_t workspace_bytes, void* hip_stream);
+
+/*
  * rtl_sparse_linear_compressed - the structured-sparse GEMM on an activation
  * already compressed in the canonical format of rtl_sparsify_2of4 (compress
  * once, multiply by any number of weights; also the unfused form of the layer,

@@ -226,3 +226,24 @@ def test_compressed_without_device():
     need = rtl.lib().rtl_sparse_linear_workspace_bytes(64, 256, 0)
     assert _cl(wsb=need) == NODEV
     assert _cl(wsb=need - 1) == WS
+
+
+def _pv(x=P, a=P2, m=64, k=256, r=8, alpha=1.0, variant=0x6, ws=WSP, wsb=BIG, stream=None):
+    return rtl.lib().rtl_sparse_linear_prepare_variant(x, a, m, k, r, alpha, variant, ws, wsb, stream)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(variant=0x10), FLAGS), (dict(variant=0xC), FLAGS), (dict(variant=0x80000000), FLAGS),
+    (dict(k=6), SHAPE), (dict(r=129), SHAPE), (dict(x=None), NULLP), (dict(a=None), NULLP),
+    (dict(x=P + 8), MISAL), (dict(ws=None), WS), (dict(wsb=16), WS), (dict(m=0), OK),
+])
+def test_prepare_variant_rejects_invalid_arguments(kw, status):
+    assert _pv(**kw) == status
+
+
+def test_prepare_variant_without_device():
+    if not _no_gpu():
+        pytest.skip("a GPU is present")
+    for comp in (rtl.COMP_TOKEN, rtl.COMP_NONE, rtl.COMP_TENSOR, rtl.COMP_GROUP):
+        for lora in (rtl.LORA_RESIDUAL, rtl.LORA_PRUNED, rtl.LORA_INPUT):
+            assert _pv(variant=comp | lora) == NODEV

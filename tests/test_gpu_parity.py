@@ -297,3 +297,52 @@ def test_compressed_linear_full_headline_sampled():
                                      np.random.default_rng(cfg.seed + 100).choice(cfg.m, 48, replace=False)]))
     ys = y_to_f64(y[torch.from_numpy(rows).to(DEV)])
     assert_y_close(ys, oracle.sparse_linear_ref(x[rows], w), "compressed full mlp_up (sampled rows)")
+
+
+COMP = {"token": rtl.COMP_TOKEN, "none": rtl.COMP_NONE, "tensor": rtl.COMP_TENSOR, "group": rtl.COMP_GROUP}
+LORA = {"residual": rtl.LORA_RESIDUAL, "pruned": rtl.LORA_PRUNED, "input": rtl.LORA_INPUT}
+VARIANT_SHAPES = [
+    # (M, K, N, r): DMA pre-pass with K % 128 == 0; DMA with a channel tail;
+    # the generic pre-pass for r > 64; the generic one for K % 8 == 4
+    (256, 1024, 160, 32), (300, 520, 200, 24), (64, 256, 96, 96), (33, 260, 100, 16),
+]
+
+
+@pytest.mark.parametrize("comp", list(COMP))
+@pytest.mark.parametrize("lora", list(LORA))
+def test_variants_against_oracle(comp, lora):
+    for m, k, n, r in VARIANT_SHAPES:
+        say(f"[parity] variant comp={comp} lora={lora} M={m} K={k} N={n} r={r}")
+        rng = np.random.default_rng(m + k + n + r)
+        x = gen.mixture_bernoulli(rng, m, k)
+        w = gen.gaussian_bits(rng, (n, k), 0.02)
+        a = gen.gaussian_bits(rng, (r, k), 0.05)
+        b = gen.gaussian_bits(rng, (n, r), 0.05)
+        prep = rtl.prepare(to_dev(x), to_dev(a), 0.75, variant=COMP[comp] | LORA[lora])
+        y = rtl.apply(prep, to_dev(w), to_dev(b))
+        torch.cuda.synchronize()
+        ref = oracle.sparse_linear_variant_ref(x, w, a, b, 0.75, comp=comp, lora=lora)
+        assert_y_close(y_to_f64(y), ref, f"comp={comp} lora={lora} {(m, k, n, r)}")
+
+
+def test_variant_tensor_and_group_full_headline_sampled():
+    cfg = gen.config("mlp_up")
+    x, w, a, b = gen.make_config("mlp_up")
+    xd, wd, ad, bd = to_dev(x), to_dev(w), to_dev(a), to_dev(b)
+    rows = np.unique(np.concatenate([np.arange(4), cfg.m - 1 - np.arange(4),
+                                     np.random.default_rng(cfg.seed + 200).choice(cfg.m, 24, replace=False)]))
+    for comp in ("tensor", "group"):
+        say(f"[parity] full mlp_up variant comp={comp}")
+        y = rtl.apply(rtl.prepare(xd, ad, 1.0, variant=COMP[comp]), wd, bd)
+        torch.cuda.synchronize()
+        ys = y_to_f64(y[torch.from_numpy(rows).to(DEV)])
+        if comp == "tensor":
+            # the factor comes from the whole X: take it from the oracle on all
+            # rows, then the sampled rows' product
+            sx, _ = oracle.sparsify_variant(x, "tensor")
+            xf = oracle.bf16_bits_to_f64(x)
+            f = oracle.bf16_bits_to_f64
+            ref = sx[rows] @ f(w).T + ((xf[rows] - sx[rows]) @ f(a).T) @ f(b).T
+        else:
+            ref = oracle.sparse_linear_variant_ref(x[rows], w, a, b, 1.0, comp="group")
+        assert_y_close(ys, ref, f"full mlp_up comp={comp} (sampled rows)")
