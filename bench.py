@@ -327,6 +327,75 @@ def run_suite(reps: int, warmup: int):
                       "speedup_vs_hipblaslt": round(tot_b / tot_s, 3)}), flush=True)
 
 
+def run_variants(reps: int, warmup: int):
+    """The compensation and LoRA-input variants: for every workload, the
+    relative rms deviation of Y from the dense product X W^T (the quantity
+    the compensation is meant to shrink) with r = 0; then on the headline
+    all 12 variants with its rank-64 LoRA (random factors: the branch adds a
+    term here instead of restoring one), with their times.  One JSON line
+    each.  The deviation is measured with torch on the device, in fp32."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gemm_token_amd as rtl
+    from workloads import gen
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    comps = {"token": rtl.COMP_TOKEN, "none": rtl.COMP_NONE, "tensor": rtl.COMP_TENSOR, "group": rtl.COMP_GROUP}
+    loras = {"residual": rtl.LORA_RESIDUAL, "pruned": rtl.LORA_PRUNED, "input": rtl.LORA_INPUT}
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def rel_dev(y, yd):
+        d = (y.float() - yd.float()).pow(2).mean().sqrt()
+        return float(d / yd.float().pow(2).mean().sqrt())
+
+    def mean_ms(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for name in SUITE:
+        cfg = gen.config(name)
+        x, w, _, _ = gen.make_config(cfg, with_lora=False)
+        xd, wd = up(x), up(w)
+        yd = rtl.dense_linear(xd, wd)
+        ws = torch.empty((rtl.sparse_linear_workspace_bytes(cfg.m, cfg.k, 0),), dtype=torch.uint8, device=dev)
+        line = {"workload": name, "r": 0, "x_law": cfg.x_law}
+        for cn, cv in comps.items():
+            y = rtl.apply(rtl.prepare(xd, None, 1.0, workspace=ws, variant=cv), wd)
+            line[f"dev_{cn}"] = round(rel_dev(y, yd), 5)
+        print(json.dumps(line), flush=True)
+        del xd, wd, yd, ws
+
+    cfg = gen.config("mlp_up")
+    x, w, a, b = gen.make_config(cfg)
+    xd, wd, ad, bd = up(x), up(w), up(a), up(b)
+    yd = rtl.dense_linear(xd, wd)
+    y = torch.empty_like(yd)
+    ws = torch.empty((rtl.sparse_linear_workspace_bytes(cfg.m, cfg.k, cfg.r),), dtype=torch.uint8, device=dev)
+    for cn, cv in comps.items():
+        for ln, lv in loras.items():
+            v = cv | lv
+            t_prep = mean_ms(lambda: rtl.prepare(xd, ad, 1.0, workspace=ws, variant=v))
+            p = rtl.prepare(xd, ad, 1.0, workspace=ws, variant=v)
+            t_app = mean_ms(lambda: rtl.apply(p, wd, bd, out=y))
+            rtl.apply(p, wd, bd, out=y)
+            print(json.dumps({"workload": "mlp_up", "r": cfg.r, "comp": cn, "lora": ln,
+                              "prepare_us": round(t_prep * 1e3, 2), "apply_us": round(t_app * 1e3, 2),
+                              "dev_vs_dense": round(rel_dev(y, yd), 5)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -343,6 +412,8 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_sparse_gemm_<workload>.json from the two rocprofv3 --pmc "
                          "output folders of --counters runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--variants", action="store_true",
+                    help="deviation from the dense product and time of every compensation / LoRA-input variant")
     ap.add_argument("--suite", action="store_true",
                     help="time every linear-layer workload and one DiT block's linears; one JSON line each")
     args = ap.parse_args()
@@ -359,6 +430,9 @@ def main():
         sys.exit(2)
     if args.suite:
         run_suite(args.steps, args.warmup)
+        return
+    if args.variants:
+        run_variants(min(args.steps, 100), min(args.warmup, 100))
         return
 
     import numpy as np
