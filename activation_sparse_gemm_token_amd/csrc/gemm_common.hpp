@@ -276,13 +276,16 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[RB][CB], c
 }
 
 // Vector-memory operations (buffer stores) store_tile_via_lds_passes
-// issues per wavefront.
+// issues per wavefront: per pass, the 16 PRB x 2 CB chunks of 16 bytes,
+// 64 per store.
 template <int RB, int CB, int PRB>
-constexpr int store_passes_ops() { return (RB / PRB) * (16 * PRB / (64 / (2 * CB))); }
+constexpr int store_passes_ops() { return (RB / PRB) * ((16 * PRB * 2 * CB + 63) / 64); }
 
 // The same store in passes of PRB row blocks through a smaller region
 // (16 PRB rows x store_pitch<CB>() bytes per wavefront at `region`), for a
-// persistent kernel whose ring keeps the next tile's copies in flight.
+// persistent kernel whose ring keeps the next tile's copies in flight.  The
+// read-back walks the pass's (row, 16-byte chunk) items 64 at a time, so any
+// CB works (2 CB chunks per row need not divide 64).
 template <int RB, int CB, int PRB>
 __device__ __forceinline__ void store_tile_via_lds_passes(const f32x4 (&acc)[RB][CB], char* region,
                                                           uint16_t* __restrict__ y, int64_t M, int64_t N,
@@ -290,13 +293,10 @@ __device__ __forceinline__ void store_tile_via_lds_passes(const f32x4 (&acc)[RB]
   static_assert(RB % PRB == 0, "whole passes");
   constexpr int kPitch = store_pitch<CB>();
   constexpr int kChunks = 2 * CB;                  // 16-byte chunks per row
-  constexpr int kRowsPerPass = 64 / kChunks;
+  constexpr int kItems = 16 * PRB * kChunks;       // per pass
+  constexpr int kIters = (kItems + 63) / 64;
   const int lane = threadIdx.x & 63;
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, M * N * 2);
-  const int sub_row = lane / kChunks, chunk = lane % kChunks;
-  const int64_t col = n0 + 8 * chunk;
-  const bool col_ok = col + 8 <= N;
-  const uint32_t pass_bytes = (uint32_t)(kRowsPerPass * N * 2);
 #pragma unroll
   for (int pass = 0; pass < RB / PRB; ++pass) {
 #pragma unroll
@@ -314,14 +314,36 @@ __device__ __forceinline__ void store_tile_via_lds_passes(const f32x4 (&acc)[RB]
     // these reads.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t mp = m0 + 16 * PRB * pass;
-    const uint32_t lane_off = (uint32_t)(((mp + sub_row) * N + col) * 2);
+    if constexpr (64 % kChunks == 0) {
+      // Whole rows per store: each lane keeps its chunk (column) throughout.
+      constexpr int kRowsPerPass = 64 / kChunks;
+      const int sub_row = lane / kChunks, chunk = lane % kChunks;
+      const int64_t col = n0 + 8 * chunk;
+      const bool col_ok = col + 8 <= N;
+      const uint32_t lane_off = (uint32_t)(((mp + sub_row) * N + col) * 2);
+      const uint32_t pass_bytes = (uint32_t)(kRowsPerPass * N * 2);
 #pragma unroll
-    for (int it = 0; it < 16 * PRB / kRowsPerPass; ++it) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(region + (kRowsPerPass * it + sub_row) * kPitch + 16 * chunk);
-      const bool ok = col_ok && mp + kRowsPerPass * it + sub_row < M;
-      const uint32_t voff = ok ? lane_off + (uint32_t)it * pass_bytes : kOobOffset;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v),
-                                             yr, voff, 0, 0);
+      for (int it = 0; it < kIters; ++it) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(region + (kRowsPerPass * it + sub_row) * kPitch + 16 * chunk);
+        const bool ok = col_ok && mp + kRowsPerPass * it + sub_row < M;
+        const uint32_t voff = ok ? lane_off + (uint32_t)it * pass_bytes : kOobOffset;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v),
+                                               yr, voff, 0, 0);
+      }
+    } else {
+      const uint32_t pass_base = (uint32_t)(mp * N * 2), n2 = (uint32_t)(N * 2);
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int item = 64 * it + lane;
+        const int row = item / kChunks, chunk = item % kChunks;
+        const bool in = item < kItems;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(region + (in ? row * kPitch + 16 * chunk : 0));
+        const int64_t col = n0 + 8 * chunk;
+        const bool ok = in && col + 8 <= N && mp + row < M;
+        const uint32_t voff = ok ? pass_base + (uint32_t)row * n2 + (uint32_t)col * 2u : kOobOffset;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v),
+                                               yr, voff, 0, 0);
+      }
     }
   }
 }

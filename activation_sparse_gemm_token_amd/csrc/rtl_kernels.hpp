@@ -18,9 +18,12 @@ hipError_t launch_prepass(const uint16_t* x, const uint16_t* lora_a, int64_t M, 
 
 // Sparse GEMM on the compressed operand plus the scale and LoRA-up epilogue.
 // `compute_units`: the device's CU count (the persistent grid's size).
+// tile_n: 256 or 192 output columns per tile, 0 to let
+// sparse_gemm_tile_n choose (the one that fills the CUs at lower cost).
 hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const uint16_t* lora_b,
                               int64_t M, int64_t N, int64_t K, int64_t r, uint16_t* y,
-                              int compute_units, hipStream_t stream);
+                              int compute_units, hipStream_t stream, int tile_n = 0);
+int sparse_gemm_tile_n(int64_t M, int64_t N, int64_t K, int compute_units);
 
 hipError_t launch_dense_gemm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,
                              int64_t K, uint16_t* y, hipStream_t stream);

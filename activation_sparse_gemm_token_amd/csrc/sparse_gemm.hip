@@ -30,32 +30,47 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveM = 128, kWaveN = 64;
-constexpr int kRB = kWaveM / 16, kCB = kWaveN / 16;          // 8 x 4 blocks per wavefront
+constexpr int kWaveM = 128;
+constexpr int kRB = kWaveM / 16;                              // 8 row blocks per wavefront
+constexpr int kStages = 3;                                   // prefetch distance 2
 
-// Per k-step LDS stage: the W tile (32 KiB), the workgroup's 256 rows of
+// Tile of 256 rows x 64 CB columns (CB = 4: 256, the default; CB = 3: 192,
+// for widths whose 256-column tiles would leave CUs idle): 8 wavefronts in
+// a 2 (M) x 4 (N) grid of 128 x 16 CB tiles (8 x CB blocks of 16 x 16).
+//
+// Per k-step LDS stage: the W tile (CB x 8 KiB), the workgroup's 256 rows of
 // compressed A (16 x 1 KiB fragments) and their position fields (2 x 1 KiB).
 // A LoRA step puts the 256 rows of alpha T / s (16 blocks x hi, lo x 1 KiB)
-// where W goes and the 256 columns of B (16 x 1 KiB) where A goes.
-constexpr int kAStageOff = kTileBytes;
-constexpr int kIStageOff = kTileBytes + 16 * 1024;
-constexpr int kStageBytes = kTileBytes + 18 * 1024;
-constexpr int kStages = 3;                                   // prefetch distance 2
-constexpr int kScaleOff = kStages * kStageBytes;             // 2 x 256 per-token scales
-constexpr int kLdsBytes = kScaleOff + 2048;
-static_assert(kWaves * 32 * store_pitch<kCB>() <= kStageBytes, "store staging (2 row blocks) fits one stage");
-
-// Vector-memory operations every step issues per wavefront: 4 for the W
-// tile, 2 for the A fragments, 1 for the position fields (a LoRA step pads
-// to the same count, so the vmcnt waits are uniform).
-constexpr int kWOps = 32 / kWaves;
-constexpr int kStepOps = kWOps + 3;
+// at the start of the stage and the tile's columns of B (4 CB x 1 KiB) after
+// them.  Two 1 KiB buffers of per-token scales follow the stages.
+template <int CB>
+struct Tile {
+  static constexpr int kCB = CB;
+  static constexpr int kWaveN = 16 * CB;
+  static constexpr int kTileNc = 4 * kWaveN;                 // 256 or 192 columns
+  static constexpr int kWBytes = kTileNc * 128;
+  static constexpr int kAStageOff = kWBytes;
+  static constexpr int kIStageOff = kWBytes + 16 * 1024;
+  static constexpr int kLoraBOff = 32 * 1024;
+  static constexpr int kKStepBytes = kWBytes + 18 * 1024;
+  static constexpr int kLoraBytes = kLoraBOff + 4 * CB * 1024;
+  static constexpr int kStageBytes = kKStepBytes > kLoraBytes ? kKStepBytes : kLoraBytes;
+  static constexpr int kScaleOff = kStages * kStageBytes;
+  static constexpr int kLdsBytes = kScaleOff + 2048;
+  // Vector-memory operations every step issues per wavefront: CB for the W
+  // tile, 2 for the A fragments, 1 for the position fields (a LoRA step
+  // pads to the same count, so the vmcnt waits are uniform).
+  static constexpr int kWOps = CB;
+  static constexpr int kStepOps = CB + 3;
+  static_assert(kWaves * 32 * store_pitch<CB>() <= kStageBytes, "store staging (2 row blocks) fits one stage");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+};
 
 // Copies of one k-step, issued by every wavefront into the stage at LDS
-// address `stage`, 7 vector-memory operations:
-//  * its 32 rows of the W tile: 4 buffer_load_dwordx4 ... lds of 8 rows x
+// address `stage`, CB + 3 vector-memory operations:
+//  * its 8 CB rows of the W tile: CB buffer_load_dwordx4 ... lds of 8 rows x
 //    128 bytes (whole lines, swizzled as described for the W tile);
-//    per-lane row offsets w_v, w1, w2, w3 (VGPR), channel offset w_so (SGPR);
+//    per-lane row offsets w[i] (VGPR), channel offset w_so (SGPR);
 //  * A fragments 2 v and 2 v + 1 (16-token block 2 v % 8 + [0, 2) of group
 //    v / 4): one 1 KiB buffer_load_dwordx4 ... lds each, source a_so; the
 //    second uses the instruction offset 1024, which moves the global and
@@ -68,40 +83,70 @@ constexpr int kStepOps = kWOps + 3;
 // It clobbers SCC.  s_nop 4 covers a VALU write of an SGPR operand right
 // before the block.  Nothing here is visible to the compiler as a load: the
 // caller waits with explicit vmcnt counts.
+template <int CB>
 __device__ __forceinline__ void dma_kstep_asm(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t ar,
-                                              __amdgpu_buffer_rsrc_t ir, uint32_t w_v, uint32_t w1,
-                                              uint32_t w2, uint32_t w3, uint32_t w_so, uint32_t a_so,
-                                              uint32_t i_so, uint32_t va, uint32_t vi, uint32_t stage,
-                                              uint32_t lw, uint32_t la, uint32_t li) {
+                                              __amdgpu_buffer_rsrc_t ir, const uint32_t (&w)[CB],
+                                              uint32_t w_so, uint32_t a_so, uint32_t i_so, uint32_t va,
+                                              uint32_t vi, uint32_t stage, uint32_t lw, uint32_t la,
+                                              uint32_t li) {
+  static_assert(CB == 3 || CB == 4, "192- or 256-column tiles");
   uint32_t saved;
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_add_u32 m0, %[st], %[lw]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[w0], %[wr], %[wso] offen lds\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[w1], %[wr], %[wso] offen lds\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[w2], %[wr], %[wso] offen lds\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[w3], %[wr], %[wso] offen lds\n\t"
-      "s_add_u32 m0, %[st], %[la]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[va], %[ar], %[aso] offen lds\n\t"
-      "buffer_load_dwordx4 %[va], %[ar], %[aso] offen offset:1024 lds\n\t"
-      "s_add_u32 m0, %[st], %[li]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %[vi], %[ir], %[iso] offen lds\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : [w0] "v"(w_v), [w1] "v"(w1), [w2] "v"(w2), [w3] "v"(w3), [va] "v"(va), [vi] "v"(vi),
-        [wr] "s"(wr), [ar] "s"(ar), [ir] "s"(ir), [wso] "s"(w_so), [aso] "s"(a_so), [iso] "s"(i_so),
-        [st] "s"(stage), [lw] "s"(lw), [la] "s"(la), [li] "s"(li)
-      : "memory", "scc");
+  if constexpr (CB == 4) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_add_u32 m0, %[st], %[lw]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w0], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w1], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w2], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w3], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, %[st], %[la]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[va], %[ar], %[aso] offen lds\n\t"
+        "buffer_load_dwordx4 %[va], %[ar], %[aso] offen offset:1024 lds\n\t"
+        "s_add_u32 m0, %[st], %[li]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %[vi], %[ir], %[iso] offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [w0] "v"(w[0]), [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [va] "v"(va), [vi] "v"(vi),
+          [wr] "s"(wr), [ar] "s"(ar), [ir] "s"(ir), [wso] "s"(w_so), [aso] "s"(a_so), [iso] "s"(i_so),
+          [st] "s"(stage), [lw] "s"(lw), [la] "s"(la), [li] "s"(li)
+        : "memory", "scc");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_add_u32 m0, %[st], %[lw]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w0], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w1], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w2], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, %[st], %[la]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[va], %[ar], %[aso] offen lds\n\t"
+        "buffer_load_dwordx4 %[va], %[ar], %[aso] offen offset:1024 lds\n\t"
+        "s_add_u32 m0, %[st], %[li]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %[vi], %[ir], %[iso] offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [w0] "v"(w[0]), [w1] "v"(w[1]), [w2] "v"(w[2]), [va] "v"(va), [vi] "v"(vi),
+          [wr] "s"(wr), [ar] "s"(ar), [ir] "s"(ir), [wso] "s"(w_so), [aso] "s"(a_so), [iso] "s"(i_so),
+          [st] "s"(stage), [lw] "s"(lw), [la] "s"(la), [li] "s"(li)
+        : "memory", "scc");
+  }
   (void)saved;
 }
 
@@ -132,60 +177,95 @@ __device__ __forceinline__ void dma_a_tile_asm(__amdgpu_buffer_rsrc_t ar, __amdg
 
 // Copies the operands of LoRA step rs into an LDS stage: thread (wave v,
 // i < 4) moves 1 KiB of alpha T / s (16-token block 2 v + i / 2, half i % 2)
-// and thread (v, i < 2) 1 KiB of B (columns n0 + 16 (2 v + i) + [0, 16),
-// ranks 32 rs + 8 (l / 16) + [0, 8)).  B rows past N and rank chunks past r
-// carry their whole offset in the VGPR operand and read as zeros.  The
-// last B copy is issued twice, so that a LoRA step issues as many
-// vector-memory operations (7) as a k-step.
+// to the start of the stage, and thread (v, i < 2) 1 KiB of B, fragments v
+// and v + 8 of the tile's 4 CB (columns n0 + 16 f + [0, 16), ranks
+// 32 rs + 8 (l / 16) + [0, 8)) to kLoraBOff + 1 KiB f; a fragment index past
+// the tile repeats fragment v.  B rows past N and rank chunks past r carry
+// their whole offset in the VGPR operand and read as zeros.  The last copy
+// is repeated until the step has issued as many vector-memory operations
+// (OPS) as a k-step.
+template <int CB, int OPS>
 __device__ __forceinline__ void dma_lora_tile_asm(__amdgpu_buffer_rsrc_t tr, __amdgpu_buffer_rsrc_t br,
                                                   uint32_t t_block0, int64_t rsteps, int64_t rs,
                                                   int64_t N, int64_t r, int64_t n0, uint32_t lds_stage_addr) {
+  static_assert(OPS == 6 || OPS == 7, "4 + 2 copies, padded to a k-step's count");
   const int lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t blk = __builtin_amdgcn_readfirstlane((uint32_t)(rsteps * 2048));
   const uint32_t t_so = __builtin_amdgcn_readfirstlane(t_block0 + 2u * wave * blk + (uint32_t)rs * 2048u);
   const uint32_t lt = __builtin_amdgcn_readfirstlane(lds_stage_addr + wave * 4096u);
-  const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_stage_addr + kAStageOff + wave * 2048u);
+  const uint32_t f1 = wave + 8u < 4u * CB ? wave + 8u : wave;
+  const uint32_t lb0 = __builtin_amdgcn_readfirstlane(lds_stage_addr + Tile<CB>::kLoraBOff + wave * 1024u);
+  const uint32_t lb1 = __builtin_amdgcn_readfirstlane(lds_stage_addr + Tile<CB>::kLoraBOff + f1 * 1024u);
   const uint32_t vt = 16u * lane;
   const int64_t j = 32 * rs + 8 * (lane >> 4);
   uint32_t vb[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int64_t n = n0 + 16 * (2 * (int64_t)wave + i) + (lane & 15);
+    const int64_t n = n0 + 16 * (int64_t)(i == 0 ? wave : f1) + (lane & 15);
     vb[i] = (n < N && j + 8 <= r) ? (uint32_t)((n * r + j) * 2) : kOobOffset;
   }
   uint32_t saved;
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 %[sv], m0\n\t"
-      "s_mov_b32 m0, %[lt0]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vt], %[tr], %[ts0] offen lds\n\t"
-      "s_mov_b32 m0, %[lt1]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vt], %[tr], %[ts1] offen lds\n\t"
-      "s_mov_b32 m0, %[lt2]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vt], %[tr], %[ts2] offen lds\n\t"
-      "s_mov_b32 m0, %[lt3]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vt], %[tr], %[ts3] offen lds\n\t"
-      "s_mov_b32 m0, %[lb0]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vb0], %[br], 0 offen lds\n\t"
-      "s_mov_b32 m0, %[lb1]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vb1], %[br], 0 offen lds\n\t"
-      "s_mov_b32 m0, %[lb1]\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %[vb1], %[br], 0 offen lds\n\t"
-      "s_mov_b32 m0, %[sv]"
-      : [sv] "=&s"(saved)
-      : [vt] "v"(vt), [vb0] "v"(vb[0]), [vb1] "v"(vb[1]), [tr] "s"(tr), [br] "s"(br),
-        [ts0] "s"(t_so), [ts1] "s"(t_so + 1024u), [ts2] "s"(t_so + blk), [ts3] "s"(t_so + blk + 1024u),
-        [lt0] "s"(lt), [lt1] "s"(lt + 1024u), [lt2] "s"(lt + 2048u), [lt3] "s"(lt + 3072u),
-        [lb0] "s"(lb), [lb1] "s"(lb + 1024u)
-      : "memory");
+  if constexpr (OPS == 7) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[lt0]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vt], %[tr], %[ts0] offen lds\n\t"
+        "s_mov_b32 m0, %[lt1]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vt], %[tr], %[ts1] offen lds\n\t"
+        "s_mov_b32 m0, %[lt2]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vt], %[tr], %[ts2] offen lds\n\t"
+        "s_mov_b32 m0, %[lt3]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vt], %[tr], %[ts3] offen lds\n\t"
+        "s_mov_b32 m0, %[lb0]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vb0], %[br], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[lb1]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vb1], %[br], 0 offen lds\n\t"
+        "buffer_load_dwordx4 %[vb1], %[br], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [vt] "v"(vt), [vb0] "v"(vb[0]), [vb1] "v"(vb[1]), [tr] "s"(tr), [br] "s"(br),
+          [ts0] "s"(t_so), [ts1] "s"(t_so + 1024u), [ts2] "s"(t_so + blk), [ts3] "s"(t_so + blk + 1024u),
+          [lt0] "s"(lt), [lt1] "s"(lt + 1024u), [lt2] "s"(lt + 2048u), [lt3] "s"(lt + 3072u),
+          [lb0] "s"(lb0), [lb1] "s"(lb1)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[lt0]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vt], %[tr], %[ts0] offen lds\n\t"
+        "s_mov_b32 m0, %[lt1]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vt], %[tr], %[ts1] offen lds\n\t"
+        "s_mov_b32 m0, %[lt2]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vt], %[tr], %[ts2] offen lds\n\t"
+        "s_mov_b32 m0, %[lt3]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vt], %[tr], %[ts3] offen lds\n\t"
+        "s_mov_b32 m0, %[lb0]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vb0], %[br], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[lb1]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[vb1], %[br], 0 offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [vt] "v"(vt), [vb0] "v"(vb[0]), [vb1] "v"(vb[1]), [tr] "s"(tr), [br] "s"(br),
+          [ts0] "s"(t_so), [ts1] "s"(t_so + 1024u), [ts2] "s"(t_so + blk), [ts3] "s"(t_so + blk + 1024u),
+          [lt0] "s"(lt), [lt1] "s"(lt + 1024u), [lt2] "s"(lt + 2048u), [lt3] "s"(lt + 3072u),
+          [lb0] "s"(lb0), [lb1] "s"(lb1)
+        : "memory");
+  }
   (void)saved;
 }
 
@@ -221,15 +301,20 @@ __device__ __forceinline__ void dma_scale_asm(__amdgpu_buffer_rsrc_t sr, uint32_
 // RING: the LoRA-up runs as extra steps of the LDS ring (r % 8 == 0 and
 // 16-byte W rows).  Otherwise it runs in the epilogue from global memory
 // (odd ranks, K % 8 == 4: shapes outside the fast path).
-template <int KM, bool RING>
+template <int KM, bool RING, int CB>
 __global__ void __launch_bounds__(kThreads, 1)
 sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi,
                    const float* __restrict__ s, const u32x4* __restrict__ tfrag,
                    const uint16_t* __restrict__ w, const uint16_t* __restrict__ lora_b,
                    int64_t M, int64_t N, int64_t K, int64_t r, int64_t kpairs,
                    int64_t rsteps, uint16_t* __restrict__ y) {
-  static_assert(!RING || KM != kAligned8, "the ring's uniform waits need 7 operations per step");
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  static_assert(!RING || KM != kAligned8, "the ring's uniform waits need CB + 3 operations per step");
+  static_assert(CB == 4 || KM != kAligned8, "the dword tile copy moves 256 rows");
+  using T = Tile<CB>;
+  constexpr int kCB = CB, kWaveN = T::kWaveN, kTileN = T::kTileNc;
+  constexpr int kAStageOff = T::kAStageOff, kIStageOff = T::kIStageOff, kStageBytes = T::kStageBytes;
+  constexpr int kScaleOff = T::kScaleOff;
+  __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
   const int wm = wave >> 2, wn = wave & 3;
@@ -256,11 +341,11 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   const uint32_t a_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 8192));
   const uint32_t i_gstride = __builtin_amdgcn_readfirstlane((uint32_t)(ksteps * 1024));
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(&lds[0]);
-  constexpr int kOps = KM == kAligned8 ? 128 / kWaves + 3 : kStepOps;
+  constexpr int kOps = KM == kAligned8 ? 128 / kWaves + 3 : T::kStepOps;
 
   // The wavefront's share of a k-step copy: LDS offsets inside a stage and
   // per-lane source offsets (see dma_kstep_asm).
-  const uint32_t lw = __builtin_amdgcn_readfirstlane(128u * 32u * (uint32_t)wave);
+  const uint32_t lw = __builtin_amdgcn_readfirstlane(1024u * kCB * (uint32_t)wave);
   const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)kAStageOff + 2048u * (uint32_t)wave);
   const uint32_t li = __builtin_amdgcn_readfirstlane((uint32_t)kIStageOff + 256u * (uint32_t)wave);
   const uint32_t row8 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * K));
@@ -284,7 +369,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     pc_iso = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 1024) + i_wave);
     pc_tb0 = __builtin_amdgcn_readfirstlane((uint32_t)(tm * 16 * rsteps * 2048));
     pc_wso = 0;
-    pc_wv = (uint32_t)(((pc_n0 + 32 * wave + (lane >> 3)) * K) * 2) + 2u * k_lane;
+    pc_wv = (uint32_t)(((pc_n0 + 8 * kCB * wave + (lane >> 3)) * K) * 2) + 2u * k_lane;
   };
   cursor_tile(0);
   auto prefetch = [&](uint32_t st_off) {
@@ -295,15 +380,19 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
         dma_a_tile_asm(ar, ir, pc_aso, pc_iso, va, vi, st, la, li);
         dma_w_tile_dword<kWaves>(wr, N, K, pc_n0, (int64_t)pc_loc * kTileK, &lds[st_off]);
       } else {
-        uint32_t w0 = pc_wv, w1 = pc_wv + row8, w2 = pc_wv + 2 * row8, w3 = pc_wv + 3 * row8;
+        uint32_t wv[kCB];
+#pragma unroll
+        for (int q = 0; q < kCB; ++q) wv[q] = pc_wv + q * row8;
         // Channel tail (kAligned16): chunks past K point out of the buffer
         // (the range check covers the VGPR and the scalar offset together).
-        if (KM == kAligned16 && (int64_t)pc_loc * kTileK + k_lane + 8 > K)
-          w0 = w1 = w2 = w3 = kOobOffset - pc_wso;
-        dma_kstep_asm(wr, ar, ir, w0, w1, w2, w3, pc_wso, pc_aso, pc_iso, va, vi, st, lw, la, li);
+        if (KM == kAligned16 && (int64_t)pc_loc * kTileK + k_lane + 8 > K) {
+#pragma unroll
+          for (int q = 0; q < kCB; ++q) wv[q] = kOobOffset - pc_wso;
+        }
+        dma_kstep_asm<kCB>(wr, ar, ir, wv, pc_wso, pc_aso, pc_iso, va, vi, st, lw, la, li);
       }
     } else {
-      dma_lora_tile_asm(tr, br, pc_tb0, rsteps, pc_loc - ksteps, N, r, pc_n0, st);
+      if constexpr (RING) dma_lora_tile_asm<kCB, kOps>(tr, br, pc_tb0, rsteps, pc_loc - ksteps, N, r, pc_n0, st);
     }
     if (pc_loc + 1 < spt) {
       ++pc_loc;
@@ -438,7 +527,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     bf16x8 bfr[kCB];
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
-      bfr[cb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + kAStageOff + (wn * kCB + cb) * 1024));
+      bfr[cb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + T::kLoraBOff + (wn * kCB + cb) * 1024));
 #pragma unroll
     for (int hl = 0; hl < 2; ++hl) {
       bf16x8 ta[kRB];
@@ -575,34 +664,60 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
 
 }  // namespace
 
+namespace {
+
+template <int CB>
+hipError_t launch_sparse_gemm_t(const u32x4* xv, const uint16_t* xi, const float* s, const u32x4* t,
+                                const uint16_t* w, const uint16_t* lora_b, int64_t M, int64_t N, int64_t K,
+                                int64_t r, int64_t kpairs, int64_t rsteps, uint16_t* y, int64_t cus,
+                                hipStream_t stream) {
+  const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + Tile<CB>::kTileNc - 1) / Tile<CB>::kTileNc);
+  // One persistent workgroup per CU (the LDS allows one), at most one per tile.
+  const dim3 grid((unsigned)(tiles < cus ? tiles : cus)), block(kThreads);
+  // The k loop runs over the padded K (a multiple of 128): full-K mode
+  // needs K itself to be one.
+  const bool ring = r % 8 == 0;
+  if (K % 128 == 0 && ring)
+    sparse_gemm_kernel<kFullK, true, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
+  else if (K % 128 == 0)
+    sparse_gemm_kernel<kFullK, false, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
+  else if (K % 8 == 0 && ring)
+    sparse_gemm_kernel<kAligned16, true, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
+  else if (K % 8 == 0)
+    sparse_gemm_kernel<kAligned16, false, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
+  else if constexpr (CB == 4)
+    sparse_gemm_kernel<kAligned8, false, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int sparse_gemm_tile_n(int64_t M, int64_t N, int64_t K, int compute_units) {
+  // 192-column tiles when they fill the CUs in fewer tile rounds, weighed by
+  // their cost relative to a 256-column tile: the kernel is bound by its
+  // operand copies, 42 KiB per k-step against 50 KiB (0.84).
+  if (K % 8 != 0) return 256;
+  const int64_t cus = compute_units > 0 ? compute_units : 1;
+  const int64_t tiles_m = (M + kTileM - 1) / kTileM;
+  auto rounds = [&](int64_t tn) { return (tiles_m * ((N + tn - 1) / tn) + cus - 1) / cus; };
+  return rounds(192) * 84 < rounds(256) * 100 ? 192 : 256;
+}
+
 hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const uint16_t* lora_b,
                               int64_t M, int64_t N, int64_t K, int64_t r, uint16_t* y,
-                              int compute_units, hipStream_t stream) {
+                              int compute_units, hipStream_t stream, int tile_n) {
   const WsLayout L = ws_layout(M, K, r);
   const char* ws = static_cast<const char*>(workspace);
   const u32x4* xv = reinterpret_cast<const u32x4*>(ws + L.off_xv);
   const uint16_t* xi = reinterpret_cast<const uint16_t*>(ws + L.off_xi);
   const float* s = reinterpret_cast<const float*>(ws + L.off_s);
   const u32x4* t = reinterpret_cast<const u32x4*>(ws + L.off_t);
-  const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
-  // One persistent workgroup per CU (the LDS allows one), at most one per tile.
-  const int64_t cus = compute_units > 0 ? compute_units : 1;
-  const dim3 grid((unsigned)(tiles < cus ? tiles : cus)), block(kThreads);
   const int64_t kpairs = L.kp / 128, rsteps = L.rp / 32;
-  // The k loop runs over the padded K (a multiple of 128): full-K mode
-  // needs K itself to be one.
-  const bool ring = r % 8 == 0;
-  if (K % 128 == 0 && ring)
-    sparse_gemm_kernel<kFullK, true><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  else if (K % 128 == 0)
-    sparse_gemm_kernel<kFullK, false><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  else if (K % 8 == 0 && ring)
-    sparse_gemm_kernel<kAligned16, true><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  else if (K % 8 == 0)
-    sparse_gemm_kernel<kAligned16, false><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  else
-    sparse_gemm_kernel<kAligned8, false><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  return hipGetLastError();
+  const int64_t cus = compute_units > 0 ? compute_units : 1;
+  if (tile_n == 0) tile_n = sparse_gemm_tile_n(M, N, K, compute_units);
+  if (tile_n == 192 && K % 8 == 0)
+    return launch_sparse_gemm_t<3>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y, cus, stream);
+  return launch_sparse_gemm_t<4>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y, cus, stream);
 }
 
 }  // namespace rtl

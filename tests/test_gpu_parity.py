@@ -346,3 +346,22 @@ def test_variant_tensor_and_group_full_headline_sampled():
         else:
             ref = oracle.sparse_linear_variant_ref(x[rows], w, a, b, 1.0, comp="group")
         assert_y_close(ys, ref, f"full mlp_up comp={comp} (sampled rows)")
+
+
+@pytest.mark.parametrize("shape", [(4103, 520, 12248, 24), (4100, 512, 12250, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ragged_wide_tiles(shape):
+    """Large ragged layers (17 row tiles, N not a multiple of 64): these take
+    256-column tiles (the 192-column ones would need an extra round of
+    tiles), in the channel-tail and the full-K copy modes."""
+    m, k, n, r = shape
+    say(f"[parity] ragged wide M={m} K={k} N={n} r={r}")
+    rng = np.random.default_rng(m + n)
+    x = gen.mixture_bernoulli(rng, m, k)
+    w = gen.gaussian_bits(rng, (n, k), 0.02)
+    a = gen.gaussian_bits(rng, (r, k), 0.01)
+    b = gen.gaussian_bits(rng, (n, r), 0.01)
+    y = run_sparse_linear(x, w, a, b)
+    rows = np.unique(np.concatenate([np.arange(4), m - 1 - np.arange(12), rng.choice(m, 24, replace=False)]))
+    ys = y_to_f64(y[torch.from_numpy(rows).to(DEV)])
+    assert_y_close(ys, oracle.sparse_linear_ref(x[rows], w, a, b), f"ragged wide {shape} (sampled rows)")
