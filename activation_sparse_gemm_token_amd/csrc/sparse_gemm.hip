@@ -21,8 +21,6 @@
 // operands from LDS for 32 structured-sparse MFMAs; with one wavefront per
 // SIMD (a 128 x 128 tile, 25 KiB for 64 MFMAs) the LDS reads of a single
 // wavefront could not keep up with its matrix core.
-#include <type_traits>
-
 #include "gemm_common.hpp"
 #include "rtl_kernels.hpp"
 
@@ -152,65 +150,6 @@ __device__ __forceinline__ void dma_kstep_asm(__amdgpu_buffer_rsrc_t wr, __amdgp
   (void)saved;
 }
 
-// One of the CB + 3 copies of dma_kstep_asm on its own, so that a k-step's
-// copies can be spread between the MFMAs of the following step: piece
-// J < CB is W row group J, pieces CB and CB + 1 the two A fragments, piece
-// CB + 2 the position fields.  Same operands, same M0 discipline.
-template <int CB, int J>
-__device__ __forceinline__ void dma_kstep_piece_asm(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t ar,
-                                                    __amdgpu_buffer_rsrc_t ir, uint32_t wq, uint32_t w_so,
-                                                    uint32_t a_so, uint32_t i_so, uint32_t va, uint32_t vi,
-                                                    uint32_t stage, uint32_t lw, uint32_t la, uint32_t li) {
-  static_assert(J >= 0 && J < CB + 3, "piece index");
-  uint32_t saved;
-  if constexpr (J < CB) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "s_mov_b32 %[sv], m0\n\t"
-        "s_add_u32 m0, %[st], %[lx]\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
-        "s_mov_b32 m0, %[sv]"
-        : [sv] "=&s"(saved)
-        : [v] "v"(wq), [rs] "s"(wr), [so] "s"(w_so), [st] "s"(stage), [lx] "s"(lw + 1024u * J)
-        : "memory", "scc");
-  } else if constexpr (J == CB) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "s_mov_b32 %[sv], m0\n\t"
-        "s_add_u32 m0, %[st], %[lx]\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
-        "s_mov_b32 m0, %[sv]"
-        : [sv] "=&s"(saved)
-        : [v] "v"(va), [rs] "s"(ar), [so] "s"(a_so), [st] "s"(stage), [lx] "s"(la)
-        : "memory", "scc");
-  } else if constexpr (J == CB + 1) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "s_mov_b32 %[sv], m0\n\t"
-        "s_add_u32 m0, %[st], %[lx]\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %[v], %[rs], %[so] offen offset:1024 lds\n\t"
-        "s_mov_b32 m0, %[sv]"
-        : [sv] "=&s"(saved)
-        : [v] "v"(va), [rs] "s"(ar), [so] "s"(a_so), [st] "s"(stage), [lx] "s"(la)
-        : "memory", "scc");
-  } else {
-    asm volatile(
-        "s_nop 4\n\t"
-        "s_mov_b32 %[sv], m0\n\t"
-        "s_add_u32 m0, %[st], %[lx]\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dword %[v], %[rs], %[so] offen lds\n\t"
-        "s_mov_b32 m0, %[sv]"
-        : [sv] "=&s"(saved)
-        : [v] "v"(vi), [rs] "s"(ir), [so] "s"(i_so), [st] "s"(stage), [lx] "s"(li)
-        : "memory", "scc");
-  }
-  (void)saved;
-}
-
 // The A fragments and position fields of dma_kstep_asm alone (3
 // operations), for rows of W that are only 8-byte aligned (K % 8 == 4),
 // whose tile goes through the compiler-visible dword copy.
@@ -236,9 +175,8 @@ __device__ __forceinline__ void dma_a_tile_asm(__amdgpu_buffer_rsrc_t ar, __amdg
   (void)saved;
 }
 
-// Copies the operands of LoRA step rs into an LDS stage, the share of
-// wavefront role v (0..7): thread (v, i < 4) moves 1 KiB of alpha T / s
-// (16-token block 2 v + i / 2, half i % 2)
+// Copies the operands of LoRA step rs into an LDS stage: thread (wave v,
+// i < 4) moves 1 KiB of alpha T / s (16-token block 2 v + i / 2, half i % 2)
 // to the start of the stage, and thread (v, i < 2) 1 KiB of B, fragments v
 // and v + 8 of the tile's 4 CB (columns n0 + 16 f + [0, 16), ranks
 // 32 rs + 8 (l / 16) + [0, 8)) to kLoraBOff + 1 KiB f; a fragment index past
@@ -249,11 +187,10 @@ __device__ __forceinline__ void dma_a_tile_asm(__amdgpu_buffer_rsrc_t ar, __amdg
 template <int CB, int OPS>
 __device__ __forceinline__ void dma_lora_tile_asm(__amdgpu_buffer_rsrc_t tr, __amdgpu_buffer_rsrc_t br,
                                                   uint32_t t_block0, int64_t rsteps, int64_t rs,
-                                                  int64_t N, int64_t r, int64_t n0, uint32_t lds_stage_addr,
-                                                  uint32_t role) {
+                                                  int64_t N, int64_t r, int64_t n0, uint32_t lds_stage_addr) {
   static_assert(OPS == 6 || OPS == 7, "4 + 2 copies, padded to a k-step's count");
   const int lane = threadIdx.x & 63;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(role);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t blk = __builtin_amdgcn_readfirstlane((uint32_t)(rsteps * 2048));
   const uint32_t t_so = __builtin_amdgcn_readfirstlane(t_block0 + 2u * wave * blk + (uint32_t)rs * 2048u);
   const uint32_t lt = __builtin_amdgcn_readfirstlane(lds_stage_addr + wave * 4096u);
@@ -435,18 +372,6 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     pc_wv = (uint32_t)(((pc_n0 + 8 * kCB * wave + (lane >> 3)) * K) * 2) + 2u * k_lane;
   };
   cursor_tile(0);
-  auto advance = [&]() {
-    if (pc_loc + 1 < spt) {
-      ++pc_loc;
-      pc_wso += 2u * kTileK;
-      pc_aso += 8192u;
-      pc_iso += 1024u;
-    } else if (pc_i + 1 < my_tiles) {
-      ++pc_i;
-      pc_loc = 0;
-      cursor_tile(pc_i);
-    }
-  };
   auto prefetch = [&](uint32_t st_off) {
     const uint32_t st = lds_base + st_off;
     const bool kcopy = !RING || pc_loc < ksteps;
@@ -467,45 +392,17 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
         dma_kstep_asm<kCB>(wr, ar, ir, wv, pc_wso, pc_aso, pc_iso, va, vi, st, lw, la, li);
       }
     } else {
-      if constexpr (RING) dma_lora_tile_asm<kCB, kOps>(tr, br, pc_tb0, rsteps, pc_loc - ksteps, N, r, pc_n0, st, wave);
+      if constexpr (RING) dma_lora_tile_asm<kCB, kOps>(tr, br, pc_tb0, rsteps, pc_loc - ksteps, N, r, pc_n0, st);
     }
-    advance();
-  };
-
-  // Spread copies.  All 8 wavefronts issuing a step's CB + 3 copies at once
-  // right after the barrier stall in the issue of the vector-memory
-  // instructions (the address unit's queue is full) for hundreds of cycles,
-  // both wavefronts of a SIMD at the same time, and the matrix core idles.
-  // Instead a k-step's refill is captured at that point (arm) and its copies
-  // go out one at a time between the MFMAs of the following k-step
-  // (piece_at), all before that step's barrier, so the vmcnt waits are the
-  // same as for the burst.
-  // (Whole k-steps only: the channel tail of kAligned16 keeps the burst.)
-  uint32_t pd_wv = 0, pd_wso = 0, pd_aso = 0, pd_iso = 0, pd_st = 0;
-  auto arm = [&](uint32_t st_off) {
-    pd_st = __builtin_amdgcn_readfirstlane(lds_base + st_off);
-    pd_wv = pc_wv;
-    pd_wso = pc_wso;
-    pd_aso = pc_aso;
-    pd_iso = pc_iso;
-    advance();
-  };
-  auto piece = [&](auto jc) {
-    constexpr int J = decltype(jc)::value;
-    if constexpr (KM == kFullK && J < kOps)
-      dma_kstep_piece_asm<kCB, J>(wr, ar, ir, pd_wv + (J < kCB ? J : 0) * row8, pd_wso, pd_aso, pd_iso, va, vi,
-                                  pd_st, lw, la, li);
-  };
-  auto piece_at = [&](int j) {
-    switch (j) {
-      case 0: piece(std::integral_constant<int, 0>{}); break;
-      case 1: piece(std::integral_constant<int, 1>{}); break;
-      case 2: piece(std::integral_constant<int, 2>{}); break;
-      case 3: piece(std::integral_constant<int, 3>{}); break;
-      case 4: piece(std::integral_constant<int, 4>{}); break;
-      case 5: piece(std::integral_constant<int, 5>{}); break;
-      case 6: piece(std::integral_constant<int, 6>{}); break;
-      default: break;
+    if (pc_loc + 1 < spt) {
+      ++pc_loc;
+      pc_wso += 2u * kTileK;
+      pc_aso += 8192u;
+      pc_iso += 1024u;
+    } else if (pc_i + 1 < my_tiles) {
+      ++pc_i;
+      pc_loc = 0;
+      cursor_tile(pc_i);
     }
   };
   // Per-token scales of tile i into LDS buffer i % 2.
@@ -578,15 +475,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   // The last column block runs after the step's barrier, together with the
   // reads of the next step's first operands and the refill (deferred to the
   // epilogue on a tile's last step, whose stage the epilogue uses).
-  //
-  // PIECES: the previous k-step armed its refill; its copies go out here,
-  // spread over the MFMA pairs of the first CB - 1 column blocks.
-  // arm_next: this step's refill is armed instead of issued (the step after
-  // is then a PIECES k-step).
-  constexpr int kSlots = (kCB - 1) * (kRB / 2);
-  static_assert(KM != kFullK || kOps <= kSlots, "one copy per MFMA pair at most");
-  auto kstep = [&](auto pieces_c, int64_t scales_for, bool after_stores, bool defer, bool arm_next) {
-    constexpr bool PIECES = decltype(pieces_c)::value;
+  auto kstep = [&](int64_t scales_for, bool after_stores, bool defer) {
     const char* s0 = b_base0 + o_cur;
     const char* s1 = b_base1 + o_cur;
     const uint32_t on = o_nxt;
@@ -598,21 +487,8 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
         bq1 = *reinterpret_cast<const u32x4*>(s1 + (cb + 1) * 2048);
 #pragma unroll
         for (int rb = 0; rb < kRB; rb += 2) {
-          if constexpr (PIECES) asm volatile("" : "+v"(acc[rb][cb]), "+v"(acc[rb + 1][cb]));
           acc[rb][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb], bf, acc[rb][cb], (int)iw[rb / 2], 0, 0);
           acc[rb + 1][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb + 1], bf, acc[rb + 1][cb], (int)iw[rb / 2], 0, 1);
-          if constexpr (PIECES) asm volatile("" : "+v"(acc[rb][cb]), "+v"(acc[rb + 1][cb]));
-          if constexpr (PIECES) {
-            // Copies [ceil(slot P / S), ceil((slot + 1) P / S)) go after MFMA
-            // pair `slot` (P copies over S pairs).
-            const int slot = cb * (kRB / 2) + rb / 2;
-#pragma unroll
-            for (int j = (slot * kOps + kSlots - 1) / kSlots; j < ((slot + 1) * kOps + kSlots - 1) / kSlots; ++j) {
-              __builtin_amdgcn_sched_barrier(0);
-              piece_at(j);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
         }
       } else {
         step_barrier(after_stores);
@@ -636,13 +512,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (arm_next) {
-          arm(o_cur);
-          if (scales_for >= 0) copy_scales(scales_for);
-          __builtin_amdgcn_sched_barrier(0);
-        } else if (!defer) {
-          refill(scales_for);
-        }
+        if (!defer) refill(scales_for);
       }
     }
     if (defer && scales_for >= 0) copy_scales(scales_for);
@@ -705,20 +575,10 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     // step leaves its refill to the epilogue.
     const int64_t next_scales = i + 1 < my_tiles ? i + 1 : -1;
     const bool after_stores = i > 0 && N % 8 == 0;
-    // Step ks arms its refill when the copy is a k-step of this tile
-    // (ks + 3 < ksteps); the steps after an armed one issue its copies.
-    constexpr bool kSpread = KM == kFullK;
-    const std::integral_constant<bool, false> burst{};
-    kstep(burst, next_scales, after_stores, lsteps == 0 && ksteps == 1, kSpread && ksteps > 3);
-    if constexpr (kSpread) {
+    kstep(next_scales, after_stores, lsteps == 0 && ksteps == 1);
 #pragma nounroll
-      for (int ks = 1; ks < ksteps - 2; ++ks) kstep(std::integral_constant<bool, true>{}, -1, false, false, ks + 3 < ksteps);
-    } else {
-#pragma nounroll
-      for (int ks = 1; ks < ksteps - 2; ++ks) kstep(burst, -1, false, false, false);
-    }
-    if (ksteps > 2) kstep(burst, -1, false, false, false);
-    if (ksteps > 1) kstep(burst, -1, false, lsteps == 0, false);
+    for (int ks = 1; ks < ksteps - 1; ++ks) kstep(-1, false, false);
+    if (ksteps > 1) kstep(-1, false, lsteps == 0);
     if constexpr (RING) {
       for (int g = 0; g < lsteps; ++g) lstep(g == lsteps - 1);
     }
