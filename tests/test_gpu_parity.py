@@ -199,6 +199,32 @@ def test_zero_rows_and_empty_calls():
     assert rtl.sparse_linear(empty, to_dev(w)).shape == (0, 64)
 
 
+def test_subnormal_and_large_magnitude_inputs():
+    """Rows of bf16 subnormals (exponent field 0), a row that mixes them with
+    normal values, and rows of magnitudes near 1e34 (the fp32 L1 sums stay
+    finite): masks bit-exact, scales within 1e-5, the layer within the
+    output bar -- over the ordinary and subnormal rows together, and over the
+    large rows on their own."""
+    rng = np.random.default_rng(43)
+    for k in (256, 1024):
+        say(f"[parity] subnormal / large magnitudes K={k}")
+        x = gen.mixture_bernoulli(rng, 48, k)
+        sub = (rng.integers(1, 128, size=(4, k)) | (rng.integers(0, 2, size=(4, k)) << 15)).astype(np.uint16)
+        x[0:4] = sub
+        x[4] = np.where(rng.random(k) < 0.5, sub[0], x[4])
+        x[8:12] = gen.f32_to_bf16_bits(rng.standard_normal((4, k)).astype(np.float32) * np.float32(1e34))
+        check_sparsify(x)
+        w = gen.gaussian_bits(rng, (200, k), 0.02)
+        a = gen.gaussian_bits(rng, (16, k), 0.01)
+        b = gen.gaussian_bits(rng, (200, 16), 0.01)
+        y = y_to_f64(run_sparse_linear(x, w, a, b))
+        ref = oracle.sparse_linear_ref(x, w, a, b)
+        big = np.arange(8, 12)
+        rest = np.setdiff1d(np.arange(48), big)
+        assert_y_close(y[rest], ref[rest], f"ordinary and subnormal rows K={k}")
+        assert_y_close(y[big], ref[big], f"rows near 1e34 K={k}")
+
+
 def test_bitwise_repeatable():
     x, w, a, b = gen.make_config("attn_proj", m=512)
     y1 = to_host(run_sparse_linear(x, w, a, b))
