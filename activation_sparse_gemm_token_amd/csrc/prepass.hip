@@ -300,14 +300,17 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
 
 // ---------------------------------------------------------------------------
 // Pre-pass with DMA-streamed operands (K % 8 == 0, 0 < r <= 64): one
-// workgroup of 4 wavefronts per 16-token block, wavefront w covering a
-// quarter of the k-steps.  Each wavefront streams its own operands into its
-// own LDS rings with buffer_load_dwordx4 ... lds (whole 128-byte lines, no
-// registers):
-//   * X: 16 tokens x 64 channels (2 KiB) per k-step, 8 stages, 7 steps ahead
-//     (HBM latency);
-//   * A: 16 NCB ranks x 64 channels (2 NCB KiB) per k-step, 3 stages, 2
-//     steps ahead (L2-resident: every workgroup reads all of A).
+// workgroup of 8 wavefronts (two per SIMD) per 16-token block, wavefront w
+// covering an eighth of the k-steps.  Each wavefront streams its own
+// operands into its own LDS rings with buffer_load_dwordx4 ... lds (whole
+// 128-byte lines, no registers):
+//   * X: 16 tokens x 64 channels (2 KiB) per k-step, 2 stages, 1 step ahead;
+//   * A: 16 NCB ranks x 64 channels (2 NCB KiB) per k-step, 2 stages, 1 step
+//     ahead (L2-resident: every workgroup reads all of A).
+// The rings fill the 160 KiB of LDS.  Two wavefronts per SIMD hide each
+// other's copy and selection latencies better than one wavefront with deep
+// rings (4 wavefronts with X 7 steps and A 2 steps ahead: 12 % slower at
+// K = 3072, 10 % at K = 12288; 5, 6 or 7 wavefronts: slower still).
 // Both tiles use the swizzled row-major layout of the GEMM's W tile
 // (16-byte chunk c of row n in slot c ^ (n & 7)), so the copies read whole
 // lines and the fragment reads are conflict-free.  Only the issuing
@@ -315,9 +318,11 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
 // The loads are inline asm, invisible to the compiler; the explicit waits
 // count them exactly, together with the stores of xv and xi (the loop's only
 // other vector-memory operations).
-constexpr int kDWaves = 4;
-constexpr int kXStages = 8, kXAhead = 7;
-constexpr int kAStages = 3, kAAhead = 2;
+constexpr int kDWaves = 8;
+constexpr int kXStages = 2, kXAhead = 1;
+constexpr int kAStages = 2, kAAhead = 1;
+static_assert(kXAhead >= kAAhead && kAAhead >= 1 && kAAhead <= 2, "issue order assumed by the waits");
+static_assert(kXStages > kXAhead && kAStages > kAAhead, "a stage is refilled only after its step");
 
 // NI 1-KiB copies (8 rows x 128 bytes each): instruction i writes LDS
 // lds_addr + 1024 i (through M0) from per-lane source offsets v[i] plus the
@@ -546,20 +551,23 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
   const uint32_t si0 = (uint32_t)((((grp * ksteps + ks_begin) * 64 + lane) * 8 + sub) * 2);
 
   if (nks > 0) {
-    // Prologue in the steady-state issue order: step t issues A(t + 2), then
-    // X(t + 7); X(0..4) first, then (A(0), X(5)), (A(1), X(6)).
+    // Prologue in the steady-state issue order: step t issues
+    // A(t + kAAhead), then X(t + kXAhead); the X copies without an A copy
+    // first, then the pairs (A(i), X(kXAhead - kAAhead + i)).
     for (int i = 0; i < kXAhead - kAAhead; ++i) copy_step(i, -1);
     for (int i = 0; i < kAAhead; ++i) copy_step(kXAhead - kAAhead + i, i);
     for (int t = 0; t < nks; ++t) {
       __builtin_amdgcn_sched_barrier(0);
       copy_step(t + kXAhead, t + kAAhead);
-      // Wait for step t's copies (X(t) was issued before A(t)).  Younger
-      // than A(t): the X copy issued with it, the copies of the two steps
-      // after it (the second just issued) and the 2 stores (xv, xi) of each
-      // step since -- fewer in the first steps.  Vector-memory operations
-      // complete in issue order, so the count is exact.
-      constexpr int kC = kXOps + 2 * (kAOps + kXOps);
-      if (t >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kC + 4) : "memory");
+      // Wait for step t's copies: A(t) and X(t), whichever came last (X(t)
+      // when kXAhead == kAAhead: they go out together, A first).  Younger
+      // than it: the X copy issued with A(t) if that was a later step's,
+      // the copies of the kAAhead steps after (the last just issued) and
+      // the 2 stores (xv, xi) of each step since -- fewer in the first
+      // steps.  Vector-memory operations complete in issue order, so the
+      // count is exact.
+      constexpr int kC = (kXAhead > kAAhead ? kXOps : 0) + kAAhead * (kAOps + kXOps);
+      if (t >= kAAhead) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kC + 2 * kAAhead) : "memory");
       else if (t == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kC + 2) : "memory");
       else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kC) : "memory");
       __builtin_amdgcn_sched_barrier(0);
