@@ -99,6 +99,10 @@ SMALL_SHAPES = [
     (16, 64, 16, 32),
     (512, 3072, 520, 64),
     (33, 260, 300, 128),
+    # DMA pre-pass with fewer k-steps than wavefronts (most of them idle):
+    # whole k-steps (K = 128) and a channel tail (K = 192 in 4 steps of 64)
+    (48, 128, 72, 64),
+    (20, 192, 40, 64),
 ]
 
 
