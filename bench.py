@@ -405,7 +405,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="mlp_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=8)
+    ap.add_argument("--cpu-reps", type=int, default=12)
     ap.add_argument("--counters", action="store_true",
                     help="a short launch sequence for rocprofv3 --pmc passes: 3 x (prepare, apply, dense, "
                          "sparsify) and 3 plain 256 MiB copies (the calibration kernel); prints no JSON")
