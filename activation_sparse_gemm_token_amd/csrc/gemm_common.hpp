@@ -72,7 +72,8 @@ __device__ __forceinline__ uint32_t frag_lane_offset(int h) {
 // them with explicit vmcnt waits.  The block has no output registers -- the
 // data goes to LDS -- and writes only M0, which it saves and restores; it
 // uses no instruction that sets SCC.  s_nop 4 covers a VALU write of an
-// SGPR operand right before the block.  With guard_k, chunks past K are
+// SGPR operand right before the block, and one wait state follows every M0
+// write before the copy that reads it.  With guard_k, chunks past K are
 // pointed out of the buffer and arrive as zeros.
 template <int WAVES>
 __device__ __forceinline__ void dma_w_tile_asm(__amdgpu_buffer_rsrc_t wr, const WTileOffsets& o, int64_t K,
@@ -95,20 +96,28 @@ __device__ __forceinline__ void dma_w_tile_asm(__amdgpu_buffer_rsrc_t wr, const 
         "s_nop 4\n\t"
         "s_mov_b32 %[sv], m0\n\t"
         "s_mov_b32 m0, %[l0]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v0], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l1]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v1], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l2]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v2], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l3]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v3], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l4]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v4], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l5]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v5], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l6]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v6], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l7]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v7], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[sv]"
         : [sv] "=&s"(saved)
@@ -122,12 +131,16 @@ __device__ __forceinline__ void dma_w_tile_asm(__amdgpu_buffer_rsrc_t wr, const 
         "s_nop 4\n\t"
         "s_mov_b32 %[sv], m0\n\t"
         "s_mov_b32 m0, %[l0]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v0], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l1]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v1], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l2]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v2], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[l3]\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %[v3], %[rs], %[so] offen lds\n\t"
         "s_mov_b32 m0, %[sv]"
         : [sv] "=&s"(saved)
