@@ -18,10 +18,13 @@ namespace rtl {
 
 namespace {
 
-// 4 wavefronts (2 x 2), each 128 x 128 = 8 x 8 blocks of 16 x 16.
-constexpr int kWaves = 4;
+// 8 wavefronts (2 x 4), each 128 x 64 = 8 x 4 blocks of 16 x 16: two per
+// SIMD, so that one wave's matrix instructions run while the other waits on
+// its LDS reads or at the barrier.  (With 4 wavefronts of 128 x 128 the
+// matrix cores idled through every such wait and a step took 30 % longer.)
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveM = 128, kWaveN = 128;
+constexpr int kWaveM = 128, kWaveN = 64;
 constexpr int kRB = kWaveM / 16, kCB = kWaveN / 16;
 
 template <int KM>
@@ -36,7 +39,7 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
   char* const lds_w = lds;
   char* const lds_a = lds + kWStages * kTileBytes;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM, tiles_n = (N + kTileN - 1) / kTileN;
   int64_t tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
