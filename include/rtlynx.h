@@ -30,6 +30,10 @@
  *     allocates nothing and keeps no pointer after a call returns.
  *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronise.  Outputs must not alias inputs.
+ *   - Host threads may call the library concurrently: its only state is a
+ *     per-device record of the architecture check, written atomically.  Calls
+ *     that can run at the same time on the GPU (different streams with no
+ *     ordering between them) must not share a workspace or an output buffer.
  *   - Every base pointer must be 16-byte aligned.
  *   - The linear-layer entry points address every tensor and every workspace
  *     region with 32-bit offsets: each of X, W, Y, A, B and the workspace
