@@ -271,29 +271,29 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
       }
     }
     __syncthreads();
-    // Output fragment (rs, l): token l % 16, rank columns 32 rs + 8 (l / 16) + [0, 8).
-    const int64_t frag = threadIdx.x;
-    if (frag < rsteps * 64) {
-      const int rs = (int)(frag >> 6), fl = (int)(frag & 63);
-      const int rr = fl & 15;
-      uint32_t hi[4], lo[4];
+    // Output fragment f = 64 rs + l: token l % 16, rank columns
+    // 32 rs + 8 (l / 16) + [0, 8), stored as 4 hi words then 4 lo words;
+    // every thread forms words (word j packs columns 2 j and 2 j + 1, each
+    // summed over the wavefronts in a fixed order).
+    const int nfrag = (int)rsteps * 64;
+    uint32_t* const tw = reinterpret_cast<uint32_t*>(t_out);
+    for (int q = (int)threadIdx.x; q < 4 * nfrag; q += 64 * kWaves) {
+      const int j = q / nfrag, f = q - j * nfrag;
+      const int rs = f >> 6, fl = f & 63, rr = fl & 15;
+      float v[2];
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        float v[2];
+      for (int e = 0; e < 2; ++e) {
+        const int col = 32 * rs + 8 * (fl >> 4) + 2 * j + e;
+        float a = 0.f;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int col = 32 * rs + 8 * (fl >> 4) + j + e;
-          float a = 0.f;
-#pragma unroll
-          for (int w = 0; w < kWaves; ++w) a += red_t[w][rr][col];
-          v[e] = alpha * a / s_sh[rr];
-        }
-        const uint32_t h = pack_bf16x2(v[0], v[1]);
-        hi[j / 2] = h;
-        lo[j / 2] = pack_bf16x2(v[0] - bf16_lo_to_f32(h), v[1] - bf16_hi_to_f32(h));
+        for (int w = 0; w < kWaves; ++w) a += red_t[w][rr][col];
+        v[e] = alpha * a / s_sh[rr];
       }
-      t_out[((mb * rsteps + rs) * 2 + 0) * 64 + fl] = (u32x4){hi[0], hi[1], hi[2], hi[3]};
-      t_out[((mb * rsteps + rs) * 2 + 1) * 64 + fl] = (u32x4){lo[0], lo[1], lo[2], lo[3]};
+      const uint32_t h = pack_bf16x2(v[0], v[1]);
+      const uint32_t l = pack_bf16x2(v[0] - bf16_lo_to_f32(h), v[1] - bf16_hi_to_f32(h));
+      const int64_t o = ((mb * rsteps + rs) * 2) * 64 + fl;
+      tw[o * 4 + j] = h;
+      tw[(o + 64) * 4 + j] = l;
     }
   }
 }
@@ -643,29 +643,29 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
     }
   }
   __syncthreads();
-  // Output fragment (rs, l): token l % 16, rank columns 32 rs + 8 (l / 16) + [0, 8).
-  const int64_t frag = threadIdx.x;
-  if (frag < rsteps * 64) {
-    const int rs = (int)(frag >> 6), fl = (int)(frag & 63);
-    const int rr = fl & 15;
-    uint32_t hi[4], lo[4];
+  // Output fragment f = 64 rs + l: token l % 16, rank columns
+  // 32 rs + 8 (l / 16) + [0, 8), stored as 4 hi words then 4 lo words.  Every
+  // thread of the workgroup forms words: word j of fragment f packs columns
+  // 2 j and 2 j + 1, each summed over the wavefronts in a fixed order.
+  const int nfrag = (int)rsteps * 64;
+  uint32_t* const tw = reinterpret_cast<uint32_t*>(t_out);
+  for (int q = (int)threadIdx.x; q < 4 * nfrag; q += 64 * kDWaves) {
+    const int j = q / nfrag, f = q - j * nfrag;
+    const int rs = f >> 6, fl = f & 63, rr = fl & 15;
+    float v[2];
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      float v[2];
+    for (int e = 0; e < 2; ++e) {
+      const int col = 32 * rs + 8 * (fl >> 4) + 2 * j + e;
+      float a = 0.f;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int col = 32 * rs + 8 * (fl >> 4) + j + e;
-        float a = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < kDWaves; ++w2) a += red.t[w2][rr][col];
-        v[e] = alpha * a / red.s[rr];
-      }
-      const uint32_t h = pack_bf16x2(v[0], v[1]);
-      hi[j / 2] = h;
-      lo[j / 2] = pack_bf16x2(v[0] - bf16_lo_to_f32(h), v[1] - bf16_hi_to_f32(h));
+      for (int w2 = 0; w2 < kDWaves; ++w2) a += red.t[w2][rr][col];
+      v[e] = alpha * a / red.s[rr];
     }
-    t_out[((mb * rsteps + rs) * 2 + 0) * 64 + fl] = (u32x4){hi[0], hi[1], hi[2], hi[3]};
-    t_out[((mb * rsteps + rs) * 2 + 1) * 64 + fl] = (u32x4){lo[0], lo[1], lo[2], lo[3]};
+    const uint32_t h = pack_bf16x2(v[0], v[1]);
+    const uint32_t l = pack_bf16x2(v[0] - bf16_lo_to_f32(h), v[1] - bf16_hi_to_f32(h));
+    const int64_t o = ((mb * rsteps + rs) * 2) * 64 + fl;
+    tw[o * 4 + j] = h;
+    tw[(o + 64) * 4 + j] = l;
   }
 }
 
