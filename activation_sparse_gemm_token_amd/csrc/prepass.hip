@@ -174,30 +174,37 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
   const int64_t p_begin = (int64_t)wave * kpairs / kWaves;
   const int64_t p_end = (int64_t)(wave + 1) * kpairs / kWaves;
   // Software pipeline over the wavefront's k-pairs: the loads of k-pair
-  // p + 1 (X and the LoRA A operand) are in flight while k-pair p is
-  // selected, compressed and multiplied.
+  // p + 1 (X and, up to rank 64, the LoRA A operand) are in flight while
+  // k-pair p is selected, compressed and multiplied.  Above rank 64 two
+  // k-pairs of A operands (2 x 128 registers) do not fit beside the
+  // accumulators, nor do two of rank 64 beside the folded words of per-group
+  // compensation: A is then loaded in the k-pair's own body, four column
+  // blocks at a time.
+  constexpr bool kPrefetchA = NCB > 0 && (NCB < 4 || (NCB == 4 && !FOLD));
+  constexpr int kChunk = NCB < 4 ? NT : 4;
   uint32_t w0[8], w1[8];
-  bf16x16 bA[NT][2];
+  bf16x16 bA[kPrefetchA ? NT : 1][2];
+  auto load_a = [&](int64_t p, int c, bf16x16 (&dst)[2]) {
+    const int64_t n = c * 16 + (lane & 15);
+    dst[0] = load_b_sparse<ALIGNED16>(ar, r, K, n, 128 * p, lane);
+    dst[1] = load_b_sparse<ALIGNED16>(ar, r, K, n, 128 * p + 64, lane);
+  };
   auto load_pair = [&](int64_t p) {
     const int64_t k = 128 * p + 16 * (lane >> 4);
     load_quad<ALIGNED16>(xr, row, row_ok, k, K, w0);
     load_quad<ALIGNED16>(xr, row, row_ok, k + 64, K, w1);
-    if constexpr (NCB > 0) {
+    if constexpr (kPrefetchA) {
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        const int64_t n = c * 16 + (lane & 15);
-        bA[c][0] = load_b_sparse<ALIGNED16>(ar, r, K, n, 128 * p, lane);
-        bA[c][1] = load_b_sparse<ALIGNED16>(ar, r, K, n, 128 * p + 64, lane);
-      }
+      for (int c = 0; c < NCB; ++c) load_a(p, c, bA[c]);
     }
   };
   if (p_begin < p_end) load_pair(p_begin);
   for (int64_t p = p_begin; p < p_end; ++p) {
     uint32_t x0[8], x1[8];
-    bf16x16 b[NT][2];
+    bf16x16 b[kPrefetchA ? NT : 1][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) { x0[i] = w0[i]; x1[i] = w1[i]; }
-    if constexpr (NCB > 0) {
+    if constexpr (kPrefetchA) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c) { b[c][0] = bA[c][0]; b[c][1] = bA[c][1]; }
     }
@@ -215,20 +222,38 @@ prepass_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ lora
     xi[((grp * ksteps + ks0) * 64 + lane) * 8 + sub] = (uint16_t)q0.kcode;
     xi[((grp * ksteps + ks0 + 1) * 64 + lane) * 8 + sub] = (uint16_t)q1.kcode;
     if constexpr (NCB > 0) {
+      // Column blocks c0 .. c0 + kChunk - 1; per block the products go in
+      // the same order whichever way A arrived.
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.kept), b[c][0], tk[c], (int)q0.kcode, 0, 0);
-        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.pruned), b[c][0], tp[c], (int)q0.pcode, 0, 0);
-        tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.kept), b[c][1], tk[c], (int)q1.kcode, 0, 0);
-        tp[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.pruned), b[c][1], tp[c], (int)q1.pcode, 0, 0);
-      }
-      if (fold && lora == kLoraResidual) {
-        // R's kept part is M*X - S(X): the folded words with their sign
-        // flipped (exact) join tk.
+      for (int c0 = 0; c0 < NCB; c0 += kChunk) {
+        bf16x16 bl[kPrefetchA ? 1 : kChunk][2];
+        if constexpr (!kPrefetchA) {
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < NCB; ++c) {
-          tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, f0 ^ 0x80008000u), b[c][0], tk[c], (int)q0.kcode, 0, 0);
-          tk[c] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, f1 ^ 0x80008000u), b[c][1], tk[c], (int)q1.kcode, 0, 0);
+          for (int c = 0; c < kChunk; ++c) load_a(p, c0 + c, bl[c]);
+        }
+        auto bop = [&](int c, int h) -> const bf16x16& {
+          if constexpr (kPrefetchA) return b[c0 + c][h];
+          else return bl[c][h];
+        };
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+          f32x4& k_ = tk[c0 + c];
+          f32x4& p_ = tp[c0 + c];
+          k_ = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.kept), bop(c, 0), k_, (int)q0.kcode, 0, 0);
+          p_ = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q0.pruned), bop(c, 0), p_, (int)q0.pcode, 0, 0);
+          k_ = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.kept), bop(c, 1), k_, (int)q1.kcode, 0, 0);
+          p_ = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, q1.pruned), bop(c, 1), p_, (int)q1.pcode, 0, 0);
+        }
+        if (fold && lora == kLoraResidual) {
+          // R's kept part is M*X - S(X): the folded words with their sign
+          // flipped (exact) join tk.
+#pragma unroll
+          for (int c = 0; c < kChunk; ++c) {
+            f32x4& k_ = tk[c0 + c];
+            k_ = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, f0 ^ 0x80008000u), bop(c, 0), k_, (int)q0.kcode, 0, 0);
+            k_ = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, f1 ^ 0x80008000u), bop(c, 1), k_, (int)q1.kcode, 0, 0);
+          }
         }
       }
     }
