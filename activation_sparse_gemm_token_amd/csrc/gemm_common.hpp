@@ -2,10 +2,10 @@
 //
 // Both kernels compute a 256 x 256 output tile per workgroup and stream
 // their operands through a ring of LDS stages in 64-deep k-steps, filled
-// by direct global -> LDS copies (buffer_load ... lds).  The dense kernel
-// runs 4 wavefronts of 128 x 128, the structured-sparse one 8 wavefronts of
-// 128 x 64 (two per SIMD: one wavefront alone cannot issue LDS reads fast
-// enough to feed the structured-sparse matrix core).  The helpers below are
+// by direct global -> LDS copies (buffer_load ... lds).  Both run 8
+// wavefronts of 128 x 64 (two per SIMD: one wavefront alone cannot issue LDS
+// reads fast enough to feed the matrix core, and idles it through its own
+// waits).  The helpers below are
 // templated on the number of wavefronts WAVES that share a tile copy and on
 // the wavefront's block counts RB x CB (16 x 16 blocks).
 #pragma once

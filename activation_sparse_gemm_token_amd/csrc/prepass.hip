@@ -778,7 +778,7 @@ hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M
     tensor_scale_kernel<<<dim3(1), dim3(1024), 0, stream>>>(part, M, s, L.mp);
   }
   if constexpr (A16) {
-    // r <= 64: the DMA-streamed pre-pass, one workgroup of 4 wavefronts per
+    // r <= 64: the DMA-streamed pre-pass, one workgroup of 8 wavefronts per
     // 16-token block (same grid and mapping).
     const dim3 dblock(64 * kDWaves);
     const int64_t ksteps = L.kp / 64;
