@@ -19,7 +19,8 @@ TFLOP/s (M N K + LoRA flops); per-call median / min / p90 of the step and
 its two halves; the layer without LoRA (r = 0) and its unfused form
 (rtl_sparsify_2of4, then rtl_sparse_linear_compressed); cold timings (MALL and L2
 flushed by a 512 MB write before every call) for the layer and both dense
-GEMMs; the graphics clock the driver reports under this load and the
+GEMMs, and the same with X read back into the caches after the flush (weights
+cold, input warm); the graphics clock the driver reports under this load and the
 fractions of the peak rescaled to it; the standalone sparsify; CPU context
 (the oracle's selection step alone, NumPy fp32 dense GEMM).
 """
@@ -562,10 +563,19 @@ def main():
     # writing 512 MB; events around the call only.
     flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
 
-    def time_cold(fn, reps=30):
+    def time_cold(fn, reps=30, warm_x=False):
         out = []
         for i in range(reps):
             flush.fill_(i & 0xFF)
+            if warm_x:
+                # Weights cold, input warm: X read back into the caches
+                # (the usual case for a layer whose input the previous
+                # layer just wrote while the weights stream from HBM).
+                torch.sum(xd)
+            # A GPU-side wait (no memory traffic) while the host enqueues
+            # the call, so that the events bracket GPU time only and not
+            # the host's launch overhead of a single call.
+            torch.cuda._sleep(1 << 21)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -578,6 +588,9 @@ def main():
     cold_step = time_cold(step)
     cold_dense = time_cold(lambda: rtl.dense_linear(xd, wd, out=yd))
     cold_blas = time_cold(lambda: torch.matmul(xd, wt, out=yd))
+    wcold_step = time_cold(step, warm_x=True)
+    wcold_dense = time_cold(lambda: rtl.dense_linear(xd, wd, out=yd), warm_x=True)
+    wcold_blas = time_cold(lambda: torch.matmul(xd, wt, out=yd), warm_x=True)
     del flush
 
     # Graphics clock under this load, read from the driver while ~1 s of
@@ -659,6 +672,11 @@ def main():
             "cold_hipblaslt_us": cold_blas,
             "cold_speedup_vs_inhouse_dense": round(cold_dense["median"] / cold_step["median"], 3),
             "cold_speedup_vs_hipblaslt": round(cold_blas["median"] / cold_step["median"], 3),
+            "wcold_step_us": wcold_step,
+            "wcold_inhouse_dense_us": wcold_dense,
+            "wcold_hipblaslt_us": wcold_blas,
+            "wcold_speedup_vs_inhouse_dense": round(wcold_dense["median"] / wcold_step["median"], 3),
+            "wcold_speedup_vs_hipblaslt": round(wcold_blas["median"] / wcold_step["median"], 3),
             "sclk_mhz_observed": sclk_obs,
             "frac_dense_peak_at_sclk": round(value / peak_at_sclk, 4) if sclk else None,
             "apply_frac_peak_at_sclk": round(achieved / peak_at_sclk, 4) if sclk else None,
