@@ -427,7 +427,8 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer runs on a single MI355X; "
-              "multi-GPU runs are not part of it (see DESIGN.md on how it would shard)", file=sys.stderr)
+              "multi-GPU runs are not part of it (it would shard by token, with no communication)",
+              file=sys.stderr)
         sys.exit(2)
     if args.suite:
         run_suite(args.steps, args.warmup)

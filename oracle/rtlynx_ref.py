@@ -21,7 +21,7 @@ Sources, cited by page and section:
   the LoRA residual.
 * neuraltrendhub summary, "What the paper found": LoRA rank 64.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 
 * "Top-K" / "keep 2 of 4" ranks by magnitude |x|; ties go to the lower
   channel index, which makes the kept set unique.
@@ -273,9 +273,8 @@ def compressed_linear_ref(vals, idx, scale, w_bits, k: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# Compensation and LoRA-input variants the pages leave open (each reading is
-# listed with the default one in the design doc).  The default of every function
-# above is comp="token", lora="residual".
+# Compensation and LoRA-input variants the pages leave open.  The default of
+# every function above is comp="token", lora="residual".
 
 def round_to_bf16(v) -> np.ndarray:
     """fp64 -> nearest bf16 value (8 significant bits), ties to even, exact:

@@ -1,7 +1,7 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle on the
 same seeded inputs.
 
-Bars (written here, derived in the design doc):
+Bars (from the bf16 rounding of the output and the fp32 reductions):
 * masks / positions (idx) and unscaled compressed values: bit-exact;
 * per-token scale: |s - s_ref| <= 1e-5 s_ref;
 * layer output: |Y - Y_ref| <= 1e-2 |Y_ref| + 1e-3 rms(Y_ref), elementwise;
