@@ -103,6 +103,8 @@ SMALL_SHAPES = [
     # whole k-steps (K = 128) and a channel tail (K = 192 in 4 steps of 64)
     (48, 128, 72, 64),
     (20, 192, 40, 64),
+    # rank 128 with K % 8 == 4 over several k-pairs per pre-pass wavefront
+    (300, 2052, 200, 128),
 ]
 
 
@@ -436,8 +438,11 @@ COMP = {"token": rtl.COMP_TOKEN, "none": rtl.COMP_NONE, "tensor": rtl.COMP_TENSO
 LORA = {"residual": rtl.LORA_RESIDUAL, "pruned": rtl.LORA_PRUNED, "input": rtl.LORA_INPUT}
 VARIANT_SHAPES = [
     # (M, K, N, r): DMA pre-pass with K % 128 == 0; DMA with a channel tail;
-    # the generic pre-pass for r > 64; the generic one for K % 8 == 4
+    # the generic pre-pass for r > 64; the generic one for K % 8 == 4; the
+    # generic one loading A per k-pair (rank 128, and rank 64 with K % 8 == 4
+    # under per-group compensation) over two k-pairs per wavefront
     (256, 1024, 160, 32), (300, 520, 200, 24), (64, 256, 96, 96), (33, 260, 100, 16),
+    (200, 2052, 136, 64), (160, 2048, 120, 128),
 ]
 
 
