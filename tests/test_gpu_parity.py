@@ -105,6 +105,10 @@ SMALL_SHAPES = [
     (20, 192, 40, 64),
     # rank 128 with K % 8 == 4 over several k-pairs per pre-pass wavefront
     (300, 2052, 200, 128),
+    # one and seven tokens against the full headline weight (one row tile,
+    # 48 column tiles)
+    (1, 3072, 12288, 64),
+    (7, 3072, 12288, 64),
 ]
 
 
