@@ -325,8 +325,19 @@ def sparsify_variant(bits, comp: str = "token"):
         s = (lk_t + lp_t) / lk_t if lk_t > 0 else 1.0
         return kept * s, mask
     if comp == "group":
-        sg = group_compensation_scale(x, mask)
-        return round_to_bf16(kept * np.repeat(sg, 4, axis=1)), mask
+        # each kept value times (L1 of its group) / (L1 of its kept pair),
+        # rounded once to bf16: formed as (x * L1 group) / L1 kept, an exact
+        # product and one division, so that the rounding is that of the
+        # exact value; a zero kept pair (a zero group) keeps its zeros
+        m, k = x.shape
+        ax = np.abs(x).reshape(m, k // 4, 4)
+        lk = np.where(mask.reshape(m, k // 4, 4), ax, 0.0).sum(axis=2)
+        tot = ax.sum(axis=2)
+        lk4 = np.repeat(lk, 4, axis=1)
+        tot4 = np.repeat(tot, 4, axis=1)
+        nz = lk4 > 0
+        q = np.where(nz, kept * tot4 / np.where(nz, lk4, 1.0), kept)
+        return round_to_bf16(q), mask
     raise ValueError(comp)
 
 

@@ -455,3 +455,74 @@ def test_variant_group_scale_restores_each_group_within_rounding():
     # at most two non-zeros per group: S(X) = X exactly
     x2 = gen.at_most_two_nonzero(rng, 8, 64)
     assert np.array_equal(oracle.sparsify_variant(x2, "group")[0], oracle.bf16_bits_to_f64(x2))
+
+
+def _rne8_exact(q):
+    """Round an exact positive rational to 8 significant bits, ties to even,
+    in exact arithmetic (brute force: scale into [128, 256) by powers of 2)."""
+    from fractions import Fraction
+    e = 0
+    while q >= 256:
+        q /= 2
+        e += 1
+    while q < 128:
+        q *= 2
+        e -= 1
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return Fraction(n) * Fraction(2) ** e
+
+
+def _near_tie_groups(rng, n=1 << 20, rows=16):
+    """Groups whose folded values lie on or within 2^-20 (relative) of a bf16
+    rounding tie, found among random groups of 8-bit integers: the values
+    where the order of the roundings decides the result.  Packed as a
+    [rows, ...] bf16 array of whole groups."""
+    v = (rng.integers(1, 256, size=(n, 4)) * rng.choice([-1, 1], size=(n, 4))).astype(np.float32) / 64
+    bits = gen.f32_to_bf16_bits(v)
+    xf = oracle.bf16_bits_to_f64(bits)
+    mask, _, _ = oracle.select_2of4(bits)
+    ax = np.abs(xf)
+    lk = np.where(mask, ax, 0.0).sum(axis=1, keepdims=True)
+    tot = ax.sum(axis=1, keepdims=True)
+    f, _ = np.frexp(ax * tot / lk)
+    t = f * 256.0                                      # in [128, 256): ties at half-integers
+    near = (np.abs(t - np.floor(t) - 0.5) < 2.0 ** -12) & mask
+    sel = bits[near.any(axis=1)]
+    sel = sel[: (len(sel) // rows) * rows]
+    assert len(sel) >= 4 * rows
+    return sel.reshape(rows, -1)
+
+
+def test_variant_group_values_are_the_exactly_rounded_products():
+    """Every folded value is x (L1 of the group) / (L1 of the kept pair) as an
+    exact rational, rounded once to bf16 with ties to even: checked in exact
+    arithmetic, on random mixtures and on small integers, where products land
+    on bf16 ties and near them."""
+    from fractions import Fraction
+    rng = np.random.default_rng(25)
+    cases = [gen.mixture_bernoulli(rng, 6, 64),
+             gen.f32_to_bf16_bits(rng.integers(-300, 301, size=(8, 64)).astype(np.float32)),
+             gen.f32_to_bf16_bits((rng.integers(1, 256, size=(8, 64)) * rng.choice([-1, 1], (8, 64)))
+                                  .astype(np.float32) / 64),
+             _near_tie_groups(rng)]
+    for x in cases:
+        sx, mask = oracle.sparsify_variant(x, "group")
+        xf = oracle.bf16_bits_to_f64(x)
+        m, k = x.shape
+        for i in range(m):
+            for g in range(k // 4):
+                vals = [Fraction(float(v)) for v in xf[i, 4 * g:4 * g + 4]]
+                kept = [j for j in range(4) if mask[i, 4 * g + j]]
+                lk = sum(abs(vals[j]) for j in kept)
+                tot = sum(abs(v) for v in vals)
+                for j in range(4):
+                    got = Fraction(float(sx[i, 4 * g + j]))
+                    if j not in kept or vals[j] == 0:
+                        assert got == 0
+                        continue
+                    q = abs(vals[j]) * tot / lk
+                    want = _rne8_exact(q) * (1 if vals[j] > 0 else -1)
+                    assert got == want, (i, g, j, float(got), float(want))
