@@ -252,13 +252,37 @@ constexpr int store_pitch() { return 32 * CB + 16; }
 template <int RB, int CB>
 constexpr int store_lds_bytes(int waves) { return waves * 16 * RB * store_pitch<CB>(); }
 
+// Writes the staged region (16 ROWS rows of 2 CB 16-byte chunks at row pitch
+// store_pitch<CB>()) to Y as coalesced 16-byte buffer stores, whole rows of
+// the tile per store.
+template <int ROWS16, int CB>
+__device__ __forceinline__ void flush_staged_region(const char* region, uint16_t* __restrict__ y, int64_t M,
+                                                    int64_t N, int64_t m0, int64_t n0) {
+  constexpr int kPitch = store_pitch<CB>();
+  constexpr int kChunks = 2 * CB;                  // 16-byte chunks per row
+  constexpr int kRowsPerPass = 64 / kChunks;
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, M * N * 2);
+  const int sub_row = lane / kChunks, chunk = lane % kChunks;
+  const int64_t col = n0 + 8 * chunk;
+  const bool col_ok = col + 8 <= N;
+  const uint32_t lane_off = (uint32_t)(((m0 + sub_row) * N + col) * 2);
+  const uint32_t pass_bytes = (uint32_t)(kRowsPerPass * N * 2);
+#pragma unroll
+  for (int it = 0; it < 16 * ROWS16 / kRowsPerPass; ++it) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region + (kRowsPerPass * it + sub_row) * kPitch + 16 * chunk);
+    const bool ok = col_ok && m0 + kRowsPerPass * it + sub_row < M;
+    const uint32_t voff = ok ? lane_off + (uint32_t)it * pass_bytes : kOobOffset;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), yr,
+                                           voff, 0, 0);
+  }
+}
+
 template <int RB, int CB>
 __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[RB][CB], char* lds_base,
                                                    uint16_t* __restrict__ y, int64_t M, int64_t N,
                                                    int64_t m0, int64_t n0) {
   constexpr int kPitch = store_pitch<CB>();
-  constexpr int kChunks = 2 * CB;                  // 16-byte chunks per row
-  constexpr int kRowsPerPass = 64 / kChunks;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   char* region = lds_base + wave * 16 * RB * kPitch;
 #pragma unroll
@@ -272,20 +296,49 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[RB][CB], c
       }
   // Only this wavefront reads its region back: a wave-local LDS wait suffices.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, M * N * 2);
-  const int sub_row = lane / kChunks, chunk = lane % kChunks;
-  const int64_t col = n0 + 8 * chunk;
-  const bool col_ok = col + 8 <= N;
-  const uint32_t lane_off = (uint32_t)(((m0 + sub_row) * N + col) * 2);
-  const uint32_t pass_bytes = (uint32_t)(kRowsPerPass * N * 2);
+  flush_staged_region<RB, CB>(region, y, M, N, m0, n0);
+}
+
+// The same for accumulators of 32 x 32 blocks (v_mfma_f32_32x32x16_bf16):
+// lane l holds column l % 32 of rows 8 (i / 4) + 4 (l / 32) + i % 4, i < 16.
+// The wavefront's tile is (32 RB) x (32 CB).
+template <int RB, int CB>
+__device__ __forceinline__ void store_tile32_via_lds(const f32x16 (&acc)[RB][CB], char* lds_base,
+                                                     uint16_t* __restrict__ y, int64_t M, int64_t N,
+                                                     int64_t m0, int64_t n0) {
+  constexpr int kPitch = store_pitch<2 * CB>();
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  char* region = lds_base + wave * 32 * RB * kPitch;
 #pragma unroll
-  for (int it = 0; it < 16 * RB / kRowsPerPass; ++it) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(region + (kRowsPerPass * it + sub_row) * kPitch + 16 * chunk);
-    const bool ok = col_ok && m0 + kRowsPerPass * it + sub_row < M;
-    const uint32_t voff = ok ? lane_off + (uint32_t)it * pass_bytes : kOobOffset;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), yr,
-                                           voff, 0, 0);
-  }
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * rb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3), col = 32 * cb + (lane & 31);
+        *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * col) = (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
+      }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  flush_staged_region<2 * RB, 2 * CB>(region, y, M, N, m0, n0);
+}
+
+// Stores a wavefront's (32 RB) x (32 CB) accumulators of 32 x 32 blocks as
+// bf16, one element per lane and store (any N).
+template <int RB, int CB>
+__device__ __forceinline__ void store_acc32_bf16(const f32x16 (&acc)[RB][CB], uint16_t* __restrict__ y,
+                                                 int64_t M, int64_t N, int64_t m0, int64_t n0) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int64_t n = n0 + 32 * cb + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t m = m0 + 32 * rb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (m < M && n < N) y[m * N + n] = (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
+      }
+    }
 }
 
 // Vector-memory operations (buffer stores) store_tile_via_lds_passes

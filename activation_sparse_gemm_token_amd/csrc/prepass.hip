@@ -774,8 +774,10 @@ hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M
     // Per-token L1 pairs go to the operand region (2 M floats <= its
     // mp kp bytes), which the pre-pass overwrites afterwards.
     float* part = reinterpret_cast<float*>(ws + L.off_xv);
-    l1_rows_kernel<A16><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream>>>(x, M, K, part);
-    tensor_scale_kernel<<<dim3(1), dim3(1024), 0, stream>>>(part, M, s, L.mp);
+    hipError_t e = launch(&l1_rows_kernel<A16>, dim3((unsigned)((M + 3) / 4)), dim3(256), stream, x, M, K, part);
+    if (e != hipSuccess) return e;
+    e = launch(&tensor_scale_kernel, dim3(1), dim3(1024), stream, part, M, s, L.mp);
+    if (e != hipSuccess) return e;
   }
   if constexpr (A16) {
     // r <= 64: the DMA-streamed pre-pass, one workgroup of 8 wavefronts per
@@ -784,31 +786,27 @@ hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M
     const int64_t ksteps = L.kp / 64;
     const bool full = K % 128 == 0;
     const bool fold = comp == kCompGroup;
-#define RTL_DMA_PREPASS(NCB_, FULL_, FOLD_)                                                              \
-  prepass_dma_kernel<NCB_, FULL_, FOLD_><<<grid, dblock, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, \
-                                                                      ksteps, rsteps, comp, lora)
     if (r > 0 && ncb <= 4) {
-      if (ncb <= 2) {
-        if (full) { if (fold) RTL_DMA_PREPASS(2, true, true); else RTL_DMA_PREPASS(2, true, false); }
-        else { if (fold) RTL_DMA_PREPASS(2, false, true); else RTL_DMA_PREPASS(2, false, false); }
-      } else {
-        if (full) { if (fold) RTL_DMA_PREPASS(4, true, true); else RTL_DMA_PREPASS(4, true, false); }
-        else { if (fold) RTL_DMA_PREPASS(4, false, true); else RTL_DMA_PREPASS(4, false, false); }
-      }
-#undef RTL_DMA_PREPASS
-      return hipGetLastError();
+      using Kern = decltype(&prepass_dma_kernel<2, true, true>);
+      static constexpr Kern kDma[2][2][2] = {
+          {{&prepass_dma_kernel<2, false, false>, &prepass_dma_kernel<2, false, true>},
+           {&prepass_dma_kernel<2, true, false>, &prepass_dma_kernel<2, true, true>}},
+          {{&prepass_dma_kernel<4, false, false>, &prepass_dma_kernel<4, false, true>},
+           {&prepass_dma_kernel<4, true, false>, &prepass_dma_kernel<4, true, true>}}};
+      return launch(kDma[ncb > 2][full][fold], grid, dblock, stream, x, lora_a, M, K, r, alpha, xv, xi, s, t,
+                    ksteps, rsteps, comp, lora);
     }
   }
-#define RTL_PREPASS(NCB_, FOLD_, RS_)                                                                  \
-  prepass_kernel<A16, NCB_, FOLD_><<<grid, block, 0, stream>>>(x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs, \
-                                                               RS_, comp, lora)
   const bool fold = comp == kCompGroup;
-  if (r == 0) { if (fold) RTL_PREPASS(0, true, 0); else RTL_PREPASS(0, false, 0); }
-  else if (ncb <= 2) { if (fold) RTL_PREPASS(2, true, rsteps); else RTL_PREPASS(2, false, rsteps); }
-  else if (ncb <= 4) { if (fold) RTL_PREPASS(4, true, rsteps); else RTL_PREPASS(4, false, rsteps); }
-  else { if (fold) RTL_PREPASS(8, true, rsteps); else RTL_PREPASS(8, false, rsteps); }
-#undef RTL_PREPASS
-  return hipGetLastError();
+  using Kern = decltype(&prepass_kernel<A16, 0, false>);
+  static constexpr Kern kGen[4][2] = {
+      {&prepass_kernel<A16, 0, false>, &prepass_kernel<A16, 0, true>},
+      {&prepass_kernel<A16, 2, false>, &prepass_kernel<A16, 2, true>},
+      {&prepass_kernel<A16, 4, false>, &prepass_kernel<A16, 4, true>},
+      {&prepass_kernel<A16, 8, false>, &prepass_kernel<A16, 8, true>}};
+  const int sel = r == 0 ? 0 : ncb <= 2 ? 1 : ncb <= 4 ? 2 : 3;
+  return launch(kGen[sel][fold], grid, block, stream, x, lora_a, M, K, r, alpha, xv, xi, s, t, kpairs,
+                r == 0 ? (int64_t)0 : rsteps, comp, lora);
 }
 
 }  // namespace

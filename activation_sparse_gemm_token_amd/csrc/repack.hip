@@ -88,11 +88,8 @@ hipError_t launch_repack(const uint16_t* vals, const uint8_t* idx, const float* 
   float* s = reinterpret_cast<float*>(ws + L.off_s);
   const int64_t ngroups = L.mp / 128, ksteps = L.kp / 64;
   const dim3 grid((unsigned)(ngroups * ksteps)), block(512);
-  if (K % 16 == 0)
-    repack_kernel<true><<<grid, block, 0, stream>>>(vals, idx, scale, M, K, xv, xi, s, ksteps);
-  else
-    repack_kernel<false><<<grid, block, 0, stream>>>(vals, idx, scale, M, K, xv, xi, s, ksteps);
-  return hipGetLastError();
+  auto* k = K % 16 == 0 ? &repack_kernel<true> : &repack_kernel<false>;
+  return launch(k, grid, block, stream, vals, idx, scale, M, K, xv, xi, s, ksteps);
 }
 
 }  // namespace rtl

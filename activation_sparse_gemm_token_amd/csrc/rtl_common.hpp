@@ -4,12 +4,36 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 namespace rtl {
+
+// Host-side launch of kernel k that returns this launch's own status
+// (hipLaunchKernel), instead of reading the thread's last-error slot after a
+// triple-chevron launch: an earlier asynchronous error of the caller is then
+// neither reported as the library's failure nor cleared.  The arguments are
+// converted to the kernel's parameter types first.
+template <typename Kern, typename Tuple, size_t... I>
+inline hipError_t launch_tuple(Kern k, dim3 grid, dim3 block, hipStream_t stream, Tuple& t,
+                               std::index_sequence<I...>) {
+  void* ptrs[] = {static_cast<void*>(&std::get<I>(t))...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, 0, stream);
+}
+
+template <typename... P, typename... A>
+inline hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t stream, A&&... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<std::decay_t<P>...> args(std::forward<A>(a)...);
+  return launch_tuple(k, grid, block, stream, args, std::index_sequence_for<P...>{});
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -132,14 +156,40 @@ constexpr int kCompToken = 0, kCompNone = 1, kCompTensor = 2, kCompGroup = 3;
 // (1 - M) * X, or the whole input X.
 constexpr int kLoraResidual = 0, kLoraPruned = 1, kLoraInput = 2;
 
+// fp64 -> bf16, round to nearest even (finite inputs; values past the bf16
+// range give infinity).  Normal results round the fp64 significand at its
+// bit 45; results below 2^-126 are multiples of 2^-133, the bf16 subnormal
+// quantum.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double q) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, q);
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  const double a = __builtin_fabs(q);
+  if (a < 0x1p-126) return sign | (uint32_t)__builtin_rint(a * 0x1p133);
+  uint64_t b = u & 0x7fffffffffffffffull;
+  b += 0x00000fffffffffffull + ((b >> 45) & 1u);
+  const int64_t e = (int64_t)(b >> 52) - 1023;
+  if (e > 127) return sign | 0x7f80u;
+  return sign | ((uint32_t)(e + 127) << 7) | ((uint32_t)(b >> 45) & 0x7fu);
+}
+
 // The kept pair of one group (operand word, channel order) scaled by the
-// group's compensation factor -- L1 of the group over L1 of the kept pair,
-// 1 for a zero pair -- and rounded to bf16.
+// group's compensation factor -- L1 of the group over L1 of the kept pair --
+// and rounded to bf16 once: each value is formed as
+// (x * L1 group) / L1 kept in fp64, from the exact magnitudes, so the
+// product and the sums are exact (for magnitudes within 2^45 of each other,
+// i.e. any group but pathological ones) and the one correctly rounded
+// division makes the bf16 rounding that of the exact value.  A zero kept
+// pair (a zero group) is returned as it is.
 __device__ __forceinline__ uint32_t fold_group(uint32_t kept_word, const Group4& g) {
-  const float lkg = add_mag_pair(0.f, g.first, g.second);
-  const float lpg = add_mag_pair(0.f, g.third, g.fourth);
-  const float sg = lkg > 0.f ? (lkg + lpg) / lkg : 1.0f;
-  return pack_bf16x2(bf16_lo_to_f32(kept_word) * sg, bf16_hi_to_f32(kept_word) * sg);
+  const double a = (double)__builtin_bit_cast(float, g.first & 0xffff0000u);
+  const double b = (double)__builtin_bit_cast(float, g.second & 0xffff0000u);
+  const double c = (double)__builtin_bit_cast(float, g.third & 0xffff0000u);
+  const double d = (double)__builtin_bit_cast(float, g.fourth & 0xffff0000u);
+  const double lk = a + b;
+  if (!(lk > 0.0)) return kept_word;
+  const double tot = lk + c + d;
+  const double v0 = (double)bf16_lo_to_f32(kept_word), v1 = (double)bf16_hi_to_f32(kept_word);
+  return f64_to_bf16_rne(v0 * tot / lk) | (f64_to_bf16_rne(v1 * tot / lk) << 16);
 }
 
 // Buffer resource over a whole tensor (raw, stride 0): loads past `bytes`

@@ -1,5 +1,6 @@
 // Launch wrappers of librtlynx's kernels (internal; the public interface is
-// include/rtlynx.h).  Each returns hipGetLastError() after its launches.
+// include/rtlynx.h).  Each returns the status of its own launches (the
+// first that failed), never the thread's earlier error.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -677,17 +677,13 @@ hipError_t launch_sparse_gemm_t(const u32x4* xv, const uint16_t* xi, const float
   // The k loop runs over the padded K (a multiple of 128): full-K mode
   // needs K itself to be one.
   const bool ring = r % 8 == 0;
-  if (K % 128 == 0 && ring)
-    sparse_gemm_kernel<kFullK, true, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  else if (K % 128 == 0)
-    sparse_gemm_kernel<kFullK, false, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  else if (K % 8 == 0 && ring)
-    sparse_gemm_kernel<kAligned16, true, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  else if (K % 8 == 0)
-    sparse_gemm_kernel<kAligned16, false, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  else if constexpr (CB == 4)
-    sparse_gemm_kernel<kAligned8, false, CB><<<grid, block, 0, stream>>>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
-  return hipGetLastError();
+  using Kern = decltype(&sparse_gemm_kernel<kFullK, true, CB>);
+  Kern k = nullptr;
+  if (K % 128 == 0) k = ring ? &sparse_gemm_kernel<kFullK, true, CB> : &sparse_gemm_kernel<kFullK, false, CB>;
+  else if (K % 8 == 0) k = ring ? &sparse_gemm_kernel<kAligned16, true, CB> : &sparse_gemm_kernel<kAligned16, false, CB>;
+  else if constexpr (CB == 4) k = &sparse_gemm_kernel<kAligned8, false, CB>;
+  if (k == nullptr) return hipErrorInvalidValue;   // K % 8 == 4 takes 256-column tiles
+  return launch(k, grid, block, stream, xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
 }
 
 }  // namespace

@@ -146,11 +146,9 @@ hipError_t launch_sparsify_2of4(const uint16_t* x, int64_t M, int64_t K, uint16_
                                 uint8_t* idx, float* scale, bool fold, hipStream_t stream) {
   const dim3 grid((unsigned)((M + kWaves - 1) / kWaves)), block(64 * kWaves);
   const bool a16 = (K % 8) == 0;
-  if (a16 && !fold) sparsify_2of4_kernel<true, false><<<grid, block, 0, stream>>>(x, M, K, vals, idx, scale);
-  else if (a16 && fold) sparsify_2of4_kernel<true, true><<<grid, block, 0, stream>>>(x, M, K, vals, idx, scale);
-  else if (!fold) sparsify_2of4_kernel<false, false><<<grid, block, 0, stream>>>(x, M, K, vals, idx, scale);
-  else sparsify_2of4_kernel<false, true><<<grid, block, 0, stream>>>(x, M, K, vals, idx, scale);
-  return hipGetLastError();
+  auto* k = a16 ? (fold ? &sparsify_2of4_kernel<true, true> : &sparsify_2of4_kernel<true, false>)
+                 : (fold ? &sparsify_2of4_kernel<false, true> : &sparsify_2of4_kernel<false, false>);
+  return launch(k, grid, block, stream, x, M, K, vals, idx, scale);
 }
 
 }  // namespace rtl
