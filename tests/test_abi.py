@@ -1,5 +1,5 @@
 """The C-ABI library on the host, without a GPU: it loads, exports every
-symbol include/rtlynx.h declares, and rejects every invalid argument with its
+symbol include/*.h declares, and rejects every invalid argument with its
 documented status before any HIP call.  No kernel is launched here."""
 import ctypes
 import os
@@ -11,6 +11,8 @@ import activation_sparse_gemm_token_amd as rtl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rtlynx.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 OK, NULLP, SHAPE, MISAL, WS, NODEV, ARCH, HIP, FLAGS = range(9)
 P = 0x10000          # fake, 16-byte aligned "device" addresses: never dereferenced
@@ -23,7 +25,9 @@ BIG = 1 << 40
 
 
 def _declared_symbols():
-    text = open(HEADER).read()
+    """Every rtl_ function named in include/*.h (declarations and the
+    comments that name them)."""
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"\b(rtl_[a-z0-9_]+)\s*\(", text)))
 
 
