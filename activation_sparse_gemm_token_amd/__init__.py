@@ -13,6 +13,8 @@ Entry points (same names as the C ABI in include/rtlynx.h, without the
 * ``sparse_linear(x, w, lora_a=None, lora_b=None, lora_scale=1.0)`` -> y
 * ``prepare(x, lora_a=None, lora_scale=1.0)`` -> Prepared, ``apply(prepared, w, lora_b=None)`` -> y
   (the two halves of sparse_linear)
+* ``sparse_linear_noalloc(x, w, lora_a=None, lora_b=None, lora_scale=1.0, out=None)`` -> y
+  (no workspace: the library's fixed per-GPU scratch array)
 * ``dense_linear(x, w)`` -> y
 * ``sparse_linear_workspace_bytes(M, K, r)``
 """
@@ -24,7 +26,7 @@ import os
 __all__ = [
     "RtlError", "lib", "library_path", "sparsify_2of4", "sparse_linear", "dense_linear",
     "sparse_linear_workspace_bytes", "version", "status_string", "STATUS", "prepare", "apply", "Prepared",
-    "FOLD_SCALE", "MAX_LORA_RANK", "sparse_linear_compressed",
+    "FOLD_SCALE", "MAX_LORA_RANK", "sparse_linear_compressed", "sparse_linear_noalloc", "NOALLOC_SCRATCH_BYTES",
     "COMP_TOKEN", "COMP_NONE", "COMP_TENSOR", "COMP_GROUP", "LORA_RESIDUAL", "LORA_PRUNED", "LORA_INPUT",
 ]
 
@@ -38,6 +40,7 @@ STATUS = {
 }
 FOLD_SCALE = 0x1
 MAX_LORA_RANK = 128
+NOALLOC_SCRATCH_BYTES = 64 << 20
 # Variants of the layer (rtl_sparse_linear_prepare_variant): compensation ...
 COMP_TOKEN, COMP_NONE, COMP_TENSOR, COMP_GROUP = 0x0, 0x1, 0x2, 0x3
 # ... | LoRA input.
@@ -50,6 +53,8 @@ _SIGNATURES = {
     "rtl_sparse_linear_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "rtl_sparse_linear": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                          _c_f, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "rtl_sparse_linear_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                                 _c_f, _c_vp, _c_vp]),
     "rtl_sparse_linear_prepare": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_f, _c_vp,
                                                  ctypes.c_size_t, _c_vp]),
     "rtl_sparse_linear_apply": (ctypes.c_int, [_c_vp, ctypes.c_size_t, _c_vp, _c_vp, _c_i64, _c_i64,
@@ -172,6 +177,36 @@ def sparse_linear(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.0, out=N
         lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None,
         m, n, k, r, float(lora_scale), y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "rtl_sparse_linear")
+    return y.reshape(*x.shape[:-1], n)
+
+
+def sparse_linear_noalloc(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.0, out=None):
+    """sparse_linear without a workspace (rtl_sparse_linear_noalloc): the
+    library's fixed per-GPU scratch array (NOALLOC_SCRATCH_BYTES) stands in
+    for it, so with ``out`` given nothing is allocated.  Calls that can
+    overlap on one GPU share that array and must be serialised."""
+    torch = _torch()
+    x2 = _as_2d(x, "x")
+    w2 = _as_2d(w, "w")
+    m, k = x2.shape
+    n = w2.shape[0]
+    if w2.shape[1] != k:
+        raise ValueError(f"w has {w2.shape[1]} input channels, x has {k}")
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        if lora_a is None or lora_b is None:
+            raise ValueError("lora_a and lora_b go together")
+        lora_a = _as_2d(lora_a, "lora_a")
+        lora_b = _as_2d(lora_b, "lora_b")
+        r = lora_a.shape[0]
+        if lora_a.shape[1] != k or lora_b.shape != (n, r):
+            raise ValueError(f"LoRA shapes {tuple(lora_a.shape)}, {tuple(lora_b.shape)} do not match "
+                             f"K={k}, N={n}")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x2.device)
+    st = lib().rtl_sparse_linear_noalloc(
+        x2.data_ptr(), w2.data_ptr(), lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None,
+        m, n, k, r, float(lora_scale), y.data_ptr(), _stream())
+    _check(st, "rtl_sparse_linear_noalloc")
     return y.reshape(*x.shape[:-1], n)
 
 

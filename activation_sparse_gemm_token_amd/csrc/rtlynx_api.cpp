@@ -9,6 +9,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "rtl_common.hpp"
 #include "rtl_kernels.hpp"
@@ -81,6 +82,34 @@ rtl_status check_device(int* cus = nullptr) {
 }
 
 rtl_status from_hip(hipError_t e) { return e == hipSuccess ? RTL_OK : RTL_ERR_HIP; }
+
+// Scratch of rtl_sparse_linear_noalloc: the workspace of the layer, held in
+// a device array of fixed size that each GPU running the library keeps
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it names a stand-in, not device memory): the device
+// address is read once per device with hipGetSymbolAddress, with that
+// device current, and kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[RTL_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device `dev`, or nullptr if
+// the runtime cannot provide it.
+void* scratch_address(int dev) {
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 }  // namespace
 
@@ -179,6 +208,32 @@ RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const
   if (rtl::launch_prepass(x, r > 0 ? lora_a : nullptr, M, K, r, lora_scale, workspace, stream) != hipSuccess)
     return RTL_ERR_HIP;
   return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y, cus, stream));
+}
+
+RTL_API rtl_status rtl_sparse_linear_noalloc(const uint16_t* x, const uint16_t* w, const uint16_t* lora_a,
+                                             const uint16_t* lora_b, int64_t M, int64_t N, int64_t K, int64_t r,
+                                             float lora_scale, uint16_t* y, void* hip_stream) {
+  if (!dims_ok(M, K) || N < 0 || N >= kMaxDim || r < 0 || r > RTL_MAX_LORA_RANK) return RTL_ERR_BAD_SHAPE;
+  if (!layer_sizes_ok(M, N, K, r)) return RTL_ERR_BAD_SHAPE;
+  if (M == 0 || N == 0) return RTL_OK;
+  if (x == nullptr || w == nullptr || y == nullptr) return RTL_ERR_NULL_POINTER;
+  if (r > 0 && (lora_a == nullptr || lora_b == nullptr)) return RTL_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return RTL_ERR_MISALIGNED;
+  if (r > 0 && (!aligned16(lora_a) || !aligned16(lora_b))) return RTL_ERR_MISALIGNED;
+  if (rtl::ws_layout(M, K, r).total > (size_t)RTL_NOALLOC_SCRATCH_BYTES) return RTL_ERR_WORKSPACE;
+  int cus = 0;
+  const rtl_status d = check_device(&cus);
+  if (d != RTL_OK) return d;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RTL_ERR_NO_DEVICE;
+  void* ws = scratch_address(dev);
+  if (ws == nullptr) return RTL_ERR_HIP;
+  // The pre-pass writes every workspace region the GEMM reads (all padded
+  // rows, k-steps and rank columns), so nothing needs clearing first.
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (rtl::launch_prepass(x, r > 0 ? lora_a : nullptr, M, K, r, lora_scale, ws, stream) != hipSuccess)
+    return RTL_ERR_HIP;
+  return from_hip(rtl::launch_sparse_gemm(ws, w, r > 0 ? lora_b : nullptr, M, N, K, r, y, cus, stream));
 }
 
 RTL_API rtl_status rtl_sparse_linear_compressed(const uint16_t* vals, const uint8_t* idx, const float* scale,

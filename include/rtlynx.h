@@ -136,6 +136,31 @@ rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w,
                              void* workspace, size_t workspace_bytes,
                              void* hip_stream);
 
+/* Size of the device scratch array that rtl_sparse_linear_noalloc uses in
+ * place of a caller workspace (64 MiB; one copy per GPU the library runs
+ * on, held until the process ends). */
+#define RTL_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * rtl_sparse_linear_noalloc - rtl_sparse_linear for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and errors as rtl_sparse_linear without the workspace: the
+ * workspace is a fixed device array inside the library, one per GPU,
+ * RTL_NOALLOC_SCRATCH_BYTES long.  A layer whose
+ * rtl_sparse_linear_workspace_bytes(M, K, r) exceeds that gives
+ * RTL_ERR_WORKSPACE (e.g. M = 9216, K = 3072, r = 64 needs 34 MB; M = 4096,
+ * K = 12288, r = 64 needs 58 MB).  The call allocates nothing, through HIP or
+ * otherwise.  Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents: calls that can overlap on one GPU (different streams
+ * without ordering between them, or several host threads) race on it and
+ * must be serialised by the caller.
+ */
+rtl_status rtl_sparse_linear_noalloc(const uint16_t* x, const uint16_t* w,
+                                     const uint16_t* lora_a, const uint16_t* lora_b,
+                                     int64_t M, int64_t N, int64_t K, int64_t r,
+                                     float lora_scale, uint16_t* y, void* hip_stream);
+
 /*
  * rtl_sparse_linear_prepare / rtl_sparse_linear_apply - the two halves of
  * rtl_sparse_linear, for callers that feed one activation to several weights

@@ -170,6 +170,33 @@ def test_python_wrappers_reject_bad_tensors():
         rtl.dense_linear(xb, xb)          # host tensors
 
 
+def _na(x=P, w=P2, a=P3, b=P4, m=64, n=128, k=256, r=8, alpha=1.0, y=P5, stream=None):
+    return rtl.lib().rtl_sparse_linear_noalloc(x, w, a, b, m, n, k, r, alpha, y, stream)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=6), SHAPE), (dict(m=-1), SHAPE), (dict(r=129), SHAPE),
+    (dict(x=None), NULLP), (dict(w=None), NULLP), (dict(y=None), NULLP), (dict(a=None), NULLP),
+    (dict(x=P + 8), MISAL), (dict(b=P4 + 8), MISAL), (dict(m=0), OK), (dict(n=0), OK),
+    # the layer's workspace must fit the fixed scratch array (64 MiB)
+    (dict(m=8192, k=8192, r=64), WS), (dict(m=1 << 14, k=4096, r=0), WS),
+])
+def test_noalloc_rejects_invalid_arguments(kw, status):
+    assert _na(**kw) == status
+
+
+def test_noalloc_limit_is_the_workspace_size():
+    """Largest accepted layers: workspace just within RTL_NOALLOC_SCRATCH_BYTES."""
+    lim = rtl.NOALLOC_SCRATCH_BYTES
+    assert rtl.sparse_linear_workspace_bytes(9216, 3072, 64) <= lim
+    assert rtl.sparse_linear_workspace_bytes(4096, 12288, 64) <= lim
+    assert rtl.sparse_linear_workspace_bytes(8192, 8192, 64) > lim
+    if _no_gpu():
+        assert _na(m=9216, k=3072, r=64) == NODEV
+        assert _na(m=4096, k=12288, r=64) == NODEV
+        assert _na(r=0, a=None, b=None) == NODEV
+
+
 def _pr(x=P, a=P2, m=64, k=256, r=8, alpha=1.0, ws=WSP, wsb=BIG, stream=None):
     return rtl.lib().rtl_sparse_linear_prepare(x, a, m, k, r, alpha, ws, wsb, stream)
 
