@@ -14,7 +14,11 @@ stderr.
 value = effective TFLOP/s = 2 M N K / (time per step): dense-equivalent
 flops, LoRA flops excluded from the numerator, LoRA time included.
 
-`detail` adds: speedups over the in-house dense GEMM and hipBLASLt; useful
+Before anything is timed, at least RAMP_MS of untimed layer calls bring the
+GPU clock up, whatever --warmup says (the clock needs tens of ms of load).
+
+`detail` adds: speedups over the in-house dense GEMM and hipBLASLt (the three
+timed in interleaved blocks, order rotated, medians); useful
 TFLOP/s (M N K + LoRA flops); per-call median / min / p90 of the step and
 its two halves; the layer without LoRA (r = 0) and its unfused form
 (rtl_sparsify_2of4, then rtl_sparse_linear_compressed); cold timings (MALL and L2
@@ -40,6 +44,8 @@ sys.path.insert(0, ROOT)
 METRIC = "eff. TFLOP/s + speedup vs dense bf16 GEMM, M=4096 K=3072 N=12288; %MFMA peak"
 PEAK_BF16_DENSE_TFLOPS = 2516.6      # 256 CU x 2048 MAC/clk x 2 x 2.4 GHz (AMD: 2.5 PF)
 PEAK_HBM_GBS = 8000.0
+RAMP_MS = 150.0         # untimed load before any timed loop (the clock's ramp)
+BLOCKS = 6              # interleaved timing blocks per leg for the speedups
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "activation_sparse_gemm_token_amd", "csrc")
 
@@ -164,11 +170,12 @@ def cpu_context(x, w):
 
 class ClockSampler:
     """Samples the graphics clock the driver reports (amdsmi GPU metrics,
-    one reading per XCD) from a host thread while a loop of steps runs."""
+    one reading per XCD) from a host thread, with host timestamps, so that
+    the readings taken while a given loop ran can be picked out."""
 
     def __init__(self):
         import threading
-        self.samples = []
+        self.samples = []                 # (perf_counter seconds, MHz)
         self._stop = threading.Event()
         self._th = None
         try:
@@ -176,7 +183,7 @@ class ClockSampler:
             amdsmi.amdsmi_init()
             self._amdsmi = amdsmi
             self._h = amdsmi.amdsmi_get_processor_handles()[0]
-        except Exception as e:          # no metrics interface: the figure is reported as null
+        except Exception as e:          # no metrics interface: the figures are reported as null
             log(f"[bench] no clock readings: {e!r}")
             self._amdsmi = None
 
@@ -186,32 +193,48 @@ class ClockSampler:
                 m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
                 c = [v for v in m.get("current_gfxclks", []) if isinstance(v, (int, float))]
                 if c:
-                    self.samples.append(sum(c) / len(c))
+                    self.samples.append((time.perf_counter(), sum(c) / len(c)))
             except Exception:
                 pass
-            self._stop.wait(0.005)
+            self._stop.wait(0.001)
 
-    def __enter__(self):
+    def start(self):
         if self._amdsmi is not None:
             import threading
             self._th = threading.Thread(target=self._run, daemon=True)
             self._th.start()
         return self
 
-    def __exit__(self, *exc):
+    def stop(self):
         if self._th is not None:
             self._stop.set()
             self._th.join()
 
-    def mhz(self):
-        """Median, min and max of the readings in the second half of the
-        loop (past the clock's ramp), or None.  The driver refreshes the
-        metrics every few hundred ms, so the loop runs for about a second."""
-        s = self.samples[len(self.samples) // 2:]
+    def window(self, t0, t1):
+        """Median, min and max of the readings taken between host times t0
+        and t1, or None if there were none."""
+        s = [v for t, v in self.samples if t0 <= t <= t1]
         if not s:
             return None
         return {"median": round(statistics.median(s), 1), "min": round(min(s), 1), "max": round(max(s), 1),
-                "distinct_readings": len(set(s))}
+                "readings": len(s)}
+
+
+def sclk_by_spin(stream, cycles: int = 1 << 20):
+    """The shader clock in MHz, measured on the GPU: torch's spin kernel
+    waits until the shader-clock counter (s_memtime) has advanced by
+    `cycles`, and events time it on `stream`.  Queued right after the timed
+    loop (outside it), it reads the clock the loop ended at (the driver's
+    own metrics refresh too slowly for a loop of a few ms; a spin queued
+    after the idle gap of a synchronize reads the clock that gap let fall).
+    Returns a lazy value (the events are read after the next sync)."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(cycles)
+    e1.record(stream)
+    return lambda: round(cycles / (e0.elapsed_time(e1) * 1e-3) / 1e6, 1)
 
 
 def dist(ms_list):
@@ -222,7 +245,8 @@ def dist(ms_list):
             "p90": round(p90 * 1e3, 2), "mean": round(sum(v) / len(v) * 1e3, 2)}
 
 
-SUITE = ("attn_proj", "mlp_up", "mlp_down", "textimg_p05", "textimg_p10", "textimg_p25")
+SUITE = ("attn_proj", "mlp_up", "mlp_down", "textimg_p05", "textimg_p10", "textimg_p25",
+         "mlp_up_share8", "textimg_share8", "textimg_share2")
 
 
 def run_suite(reps: int, warmup: int):
@@ -400,8 +424,8 @@ def run_variants(reps: int, warmup: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # Defaults: the GPU clock takes ~40 ms of sustained work to ramp up, so
-    # 300 untimed steps (~65 ms) come before 300 timed ones.
+    # The clock ramp does not depend on these (RAMP_MS of untimed calls
+    # always come first); 300 timed steps keep the event overhead small.
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="mlp_up")
@@ -476,12 +500,26 @@ def main():
         log("[bench] counter sequence done")
         return
 
+    # Clock ramp: the GPU clock needs tens of milliseconds of sustained load
+    # to reach its working frequency, so at least RAMP_MS of untimed layer
+    # calls run before anything is timed, whatever --warmup asks; then the
+    # --warmup steps.
+    clk = ClockSampler().start()
+    t_ramp0 = time.perf_counter()
+    ramp_calls = 0
+    while (time.perf_counter() - t_ramp0) * 1e3 < RAMP_MS:
+        for _ in range(25):
+            step()
+        ramp_calls += 25
+        torch.cuda.synchronize()
+    ramp_ms = (time.perf_counter() - t_ramp0) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # Timed region: K steps of rtl_sparse_linear (pre-pass + GEMM), HIP
-    # events on the launch stream around the whole loop.
+    # events on the launch stream around the whole loop; the clock readings
+    # taken meanwhile are kept.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -489,6 +527,7 @@ def main():
     for _ in range(args.steps):
         step()
     t_end.record(stream)
+    sclk_after = sclk_by_spin(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
@@ -531,11 +570,34 @@ def main():
     # path (pre-pass without LoRA-down, GEMM without LoRA-up).
     r0_ms = time_fn(lambda: rtl.sparse_linear(xd, wd, None, None, 1.0, out=y, workspace=ws), args.steps)
 
-    # In-house dense baseline and hipBLASLt (torch.matmul) for context.
+    # The speedups: the layer, the in-house dense GEMM and hipBLASLt
+    # (torch.matmul) timed in interleaved blocks of K back-to-back calls,
+    # the order rotated from block to block, so that no leg gains from
+    # coming after the others (clock, caches); medians over the blocks.
     yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-    dense_ms = time_fn(lambda: rtl.dense_linear(xd, wd, out=yd), args.steps)
     wt = wd.t()
-    blas_ms = time_fn(lambda: torch.matmul(xd, wt, out=yd), args.steps)
+    legs = {"sparse": step,
+            "dense": lambda: rtl.dense_linear(xd, wd, out=yd),
+            "hipblaslt": lambda: torch.matmul(xd, wt, out=yd)}
+    for fn in legs.values():
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    blocks = {name: [] for name in legs}
+    order = list(legs)
+    for bi in range(BLOCKS):
+        for name in order[bi % len(order):] + order[:bi % len(order)]:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                legs[name]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            blocks[name].append(e0.elapsed_time(e1) / args.steps)
+    sparse_blk_ms = statistics.median(blocks["sparse"])
+    dense_ms = statistics.median(blocks["dense"])
+    blas_ms = statistics.median(blocks["hipblaslt"])
     vals = torch.empty((m, k // 2), dtype=torch.bfloat16, device=dev)
     idx = torch.empty((m, (k // 4 + 1) // 2), dtype=torch.uint8, device=dev)
     scale = torch.empty((m,), dtype=torch.float32, device=dev)
@@ -599,12 +661,18 @@ def main():
     # nominal 2.4 GHz peak is the clock.
     for _ in range(200):
         step()
-    with ClockSampler() as clk:
-        for _ in range(max(1, int(1.0 / (ms_step * 1e-3)))):
-            step()
-        torch.cuda.synchronize()
-    sclk_obs = clk.mhz()
-    sclk = sclk_obs["median"] if sclk_obs else None
+    torch.cuda.synchronize()
+    h2 = time.perf_counter()
+    for _ in range(max(1, int(1.0 / (ms_step * 1e-3)))):
+        step()
+    torch.cuda.synchronize()
+    h3 = time.perf_counter()
+    clk.stop()
+    sclk_obs = clk.window(h2, h3)
+    # the clock the timed loop ended at, from the GPU's own counter; the
+    # driver's reading as a fallback
+    sclk_spin = sclk_after()
+    sclk = sclk_spin if sclk_spin and 500.0 < sclk_spin < 3000.0 else (sclk_obs["median"] if sclk_obs else None)
     log(f"[bench] cold step {cold_step['median']} us, dense {cold_dense['median']} us; sclk {sclk_obs} MHz")
 
     # Roofline of the dominant kernel: the structured-sparse GEMM (apply).
@@ -644,8 +712,12 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "detail": {
-            "speedup_vs_inhouse_dense": round(dense_ms / ms_step, 3),
-            "speedup_vs_hipblaslt": round(blas_ms / ms_step, 3),
+            "ramp_ms": round(ramp_ms, 1),
+            "ramp_calls": ramp_calls,
+            "speedup_vs_inhouse_dense": round(dense_ms / sparse_blk_ms, 3),
+            "speedup_vs_hipblaslt": round(blas_ms / sparse_blk_ms, 3),
+            "speedup_timing": f"medians of {BLOCKS} interleaved blocks of {args.steps} calls per leg",
+            "interleaved_us": {k: [round(v * 1e3, 2) for v in vs] for k, vs in blocks.items()},
             "inhouse_dense_tflops": round(flops_dense_eq / (dense_ms * 1e-3) / 1e12, 1),
             "hipblaslt_tflops": round(flops_dense_eq / (blas_ms * 1e-3) / 1e12, 1),
             "frac_dense_peak": round(value / PEAK_BF16_DENSE_TFLOPS, 4),
@@ -678,6 +750,7 @@ def main():
             "wcold_hipblaslt_us": wcold_blas,
             "wcold_speedup_vs_inhouse_dense": round(wcold_dense["median"] / wcold_step["median"], 3),
             "wcold_speedup_vs_hipblaslt": round(wcold_blas["median"] / wcold_step["median"], 3),
+            "sclk_mhz_after_timed_loop": sclk_spin,
             "sclk_mhz_observed": sclk_obs,
             "frac_dense_peak_at_sclk": round(value / peak_at_sclk, 4) if sclk else None,
             "apply_frac_peak_at_sclk": round(achieved / peak_at_sclk, 4) if sclk else None,

@@ -345,7 +345,8 @@ def test_concurrent_streams():
             assert np.array_equal(to_host(got), want), f"round {rep}"
 
 
-FULL = ["attn_proj", "mlp_up", "mlp_down", "textimg_p05", "textimg_p10", "textimg_p25"]
+FULL = ["attn_proj", "mlp_up", "mlp_down", "textimg_p05", "textimg_p10", "textimg_p25",
+        "mlp_up_share8", "textimg_share8", "textimg_share2"]
 
 
 def assert_all_rows_close(y_dev, ref, what, block=1024):

@@ -225,7 +225,8 @@ def test_prepass_workspace_subnormal_and_zero_rows(k, r):
     assert (scale == 1.0).all()
 
 
-FULL = ["attn_proj", "mlp_up", "mlp_down", "textimg_p05", "textimg_p10", "textimg_p25"]
+FULL = ["attn_proj", "mlp_up", "mlp_down", "textimg_p05", "textimg_p10", "textimg_p25",
+        "mlp_up_share8", "textimg_share8", "textimg_share2"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -136,6 +136,15 @@ CONFIGS = {
                           "2 x (4096 image + 512 text) tokens, 10% active"),
     "textimg_p25": Config("textimg_p25", 9216, 3072, 12288, 64, "exact", 0.25, 7,
                           "2 x (4096 image + 512 text) tokens, 25% active"),
+    # One GPU's share of a token-sharded layer (every token is independent,
+    # so a share is just a shorter call): the MLP up-projection over 8 GPUs,
+    # the text+image batch over 8 and over 2 GPUs (one image + text stream).
+    "mlp_up_share8": Config("mlp_up_share8", 512, 3072, 12288, 64, "mixture", 0.08, 8,
+                            "DiT MLP up-projection, one of 8 token shards"),
+    "textimg_share8": Config("textimg_share8", 1152, 3072, 12288, 64, "exact", 0.05, 9,
+                             "text+image batch, one of 8 token shards, 5% active"),
+    "textimg_share2": Config("textimg_share2", 4608, 3072, 12288, 64, "exact", 0.05, 10,
+                             "text+image batch, one of 2 token shards (4096 image + 512 text), 5% active"),
 }
 
 
