@@ -228,9 +228,11 @@ __device__ __forceinline__ void store_acc_bf16(const f32x4 (&acc)[RB][CB], uint1
     for (int cb = 0; cb < CB; ++cb) {
       const int64_t n = n0 + 16 * cb + (lane & 15);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; i += 2) {
+        const uint32_t p = cvt_pk_bf16(acc[rb][cb][i], acc[rb][cb][i + 1]);
         const int64_t m = m0 + 16 * rb + 4 * (lane >> 4) + i;
-        if (m < M && n < N) y[m * N + n] = (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
+        if (m < M && n < N) y[m * N + n] = (uint16_t)p;
+        if (m + 1 < M && n < N) y[(m + 1) * N + n] = (uint16_t)(p >> 16);
       }
     }
   }
@@ -290,9 +292,11 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[RB][CB], c
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; i += 2) {
         const int row = 16 * rb + 4 * (lane >> 4) + i, col = 16 * cb + (lane & 15);
-        *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * col) = (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
+        const uint32_t p = cvt_pk_bf16(acc[rb][cb][i], acc[rb][cb][i + 1]);
+        *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * col) = (uint16_t)p;
+        *reinterpret_cast<uint16_t*>(region + (row + 1) * kPitch + 2 * col) = (uint16_t)(p >> 16);
       }
   // Only this wavefront reads its region back: a wave-local LDS wait suffices.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -314,9 +318,11 @@ __device__ __forceinline__ void store_tile32_via_lds(const f32x16 (&acc)[RB][CB]
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 16; i += 2) {
         const int row = 32 * rb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3), col = 32 * cb + (lane & 31);
-        *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * col) = (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
+        const uint32_t p = cvt_pk_bf16(acc[rb][cb][i], acc[rb][cb][i + 1]);
+        *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * col) = (uint16_t)p;
+        *reinterpret_cast<uint16_t*>(region + (row + 1) * kPitch + 2 * col) = (uint16_t)(p >> 16);
       }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   flush_staged_region<2 * RB, 2 * CB>(region, y, M, N, m0, n0);
@@ -334,9 +340,11 @@ __device__ __forceinline__ void store_acc32_bf16(const f32x16 (&acc)[RB][CB], ui
     for (int cb = 0; cb < CB; ++cb) {
       const int64_t n = n0 + 32 * cb + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 16; i += 2) {
+        const uint32_t p = cvt_pk_bf16(acc[rb][cb][i], acc[rb][cb][i + 1]);
         const int64_t m = m0 + 32 * rb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (m < M && n < N) y[m * N + n] = (uint16_t)f32_to_bf16_rne(acc[rb][cb][i]);
+        if (m < M && n < N) y[m * N + n] = (uint16_t)p;
+        if (m + 1 < M && n < N) y[(m + 1) * N + n] = (uint16_t)(p >> 16);
       }
     }
 }
@@ -370,10 +378,11 @@ __device__ __forceinline__ void store_tile_via_lds_passes(const f32x4 (&acc)[RB]
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; i += 2) {
           const int row = 16 * rr + 4 * (lane >> 4) + i, c = 16 * cb + (lane & 15);
-          *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * c) =
-              (uint16_t)f32_to_bf16_rne(acc[pass * PRB + rr][cb][i]);
+          const uint32_t p = cvt_pk_bf16(acc[pass * PRB + rr][cb][i], acc[pass * PRB + rr][cb][i + 1]);
+          *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * c) = (uint16_t)p;
+          *reinterpret_cast<uint16_t*>(region + (row + 1) * kPitch + 2 * c) = (uint16_t)(p >> 16);
         }
     // Only this wavefront reads its region back; LDS operations of one
     // wavefront execute in order, so the next pass's writes cannot overtake

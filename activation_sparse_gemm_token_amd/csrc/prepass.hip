@@ -479,11 +479,16 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
   constexpr int kABytes = NCB * 2048;                 // 16 NCB ranks x 128 B
   constexpr int kWaveBytes = kXStages * kXBytes + kAStages * kABytes;
   constexpr int kXOps = 2, kAOps = 2 * NCB;
-  // Reduction arrays, aliased onto the rings after the loop.
+  // Reduction arrays, aliased onto the rings after the loop.  T rows of
+  // NCB 16 + 4 floats: the accumulator writes (four 16-lane quarters at
+  // rows 4 apart) and the epilogue's 32-byte row reads both spread over all
+  // LDS banks.
+  constexpr int kPitch = NCB * 16 + 4;
   struct Red {
     float l[kDWaves][2][16];
     float s[16];
-    float t[kDWaves][16][NCB * 16 + 1];
+    float pad[12];
+    float t[kDWaves][16][kPitch];
   };
   static_assert((int)sizeof(Red) <= kDWaves * kWaveBytes, "reduction fits in the rings");
   __shared__ __attribute__((aligned(16))) char lds[kDWaves * kWaveBytes];
@@ -669,28 +674,32 @@ prepass_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
   }
   __syncthreads();
   // Output fragment f = 64 rs + l: token l % 16, rank columns
-  // 32 rs + 8 (l / 16) + [0, 8), stored as 4 hi words then 4 lo words.  Every
-  // thread of the workgroup forms words: word j of fragment f packs columns
-  // 2 j and 2 j + 1, each summed over the wavefronts in a fixed order.
-  const int nfrag = (int)rsteps * 64;
-  uint32_t* const tw = reinterpret_cast<uint32_t*>(t_out);
-  for (int q = (int)threadIdx.x; q < 4 * nfrag; q += 64 * kDWaves) {
-    const int j = q / nfrag, f = q - j * nfrag;
-    const int rs = f >> 6, fl = f & 63, rr = fl & 15;
-    float v[2];
+  // 32 rs + 8 (l / 16) + [0, 8), four hi words then four lo words.  Thread
+  // f sums its 8 columns over the wavefronts in a fixed order (two 16-byte
+  // LDS reads per wavefront) and writes the fragment's hi and lo halves as
+  // two 16-byte stores.
+  if ((int)threadIdx.x < 64 * (int)rsteps) {
+    const int rs = threadIdx.x >> 6, fl = threadIdx.x & 63, rr = fl & 15;
+    const int col = 32 * rs + 8 * (fl >> 4);
+    f32x4 v0 = (f32x4){0, 0, 0, 0}, v1 = (f32x4){0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int col = 32 * rs + 8 * (fl >> 4) + 2 * j + e;
-      float a = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < kDWaves; ++w2) a += red.t[w2][rr][col];
-      v[e] = alpha * a / red.s[rr];
+    for (int w2 = 0; w2 < kDWaves; ++w2) {
+      v0 += *reinterpret_cast<const f32x4*>(&red.t[w2][rr][col]);
+      v1 += *reinterpret_cast<const f32x4*>(&red.t[w2][rr][col + 4]);
     }
-    const uint32_t h = pack_bf16x2(v[0], v[1]);
-    const uint32_t l = pack_bf16x2(v[0] - bf16_lo_to_f32(h), v[1] - bf16_hi_to_f32(h));
+    const float sr = red.s[rr];
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = alpha * v0[e] / sr; v[4 + e] = alpha * v1[e] / sr; }
+    u32x4 h, l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+      l[j] = pack_bf16x2(v[2 * j] - bf16_lo_to_f32(h[j]), v[2 * j + 1] - bf16_hi_to_f32(h[j]));
+    }
     const int64_t o = ((mb * rsteps + rs) * 2) * 64 + fl;
-    tw[o * 4 + j] = h;
-    tw[(o + 64) * 4 + j] = l;
+    t_out[o] = h;
+    t_out[o + 64] = l;
   }
 }
 
@@ -788,7 +797,7 @@ hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M
     const bool fold = comp == kCompGroup;
     if (r > 0 && ncb <= 4) {
       using Kern = decltype(&prepass_dma_kernel<2, true, true>);
-      static constexpr Kern kDma[2][2][2] = {
+static constexpr Kern kDma[2][2][2] = {
           {{&prepass_dma_kernel<2, false, false>, &prepass_dma_kernel<2, false, true>},
            {&prepass_dma_kernel<2, true, false>, &prepass_dma_kernel<2, true, true>}},
           {{&prepass_dma_kernel<4, false, false>, &prepass_dma_kernel<4, false, true>},

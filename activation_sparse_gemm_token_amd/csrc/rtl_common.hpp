@@ -145,6 +145,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
 }
 
+// The same rounding of two values by the hardware's packed conversion
+// (v_cvt_pk_bf16_f32, round to nearest even): a in the low half, b in the
+// high half.  One instruction instead of two per value; the GEMM epilogues
+// convert every output with it.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
