@@ -130,6 +130,38 @@ def _stream():
     return _torch().cuda.current_stream().cuda_stream
 
 
+def _out(out, m: int, n: int, lead, device):
+    """A caller's output tensor, or a new one: the kernels write m * n bf16
+    words through its data pointer, so it must be exactly that."""
+    torch = _torch()
+    if out is None:
+        return torch.empty((m, n), dtype=torch.bfloat16, device=device)
+    if out.dtype != torch.bfloat16:
+        raise TypeError(f"out must be bfloat16, got {out.dtype}")
+    if out.device != device:
+        raise ValueError(f"out is on {out.device}, the inputs on {device}")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if tuple(out.shape) not in ((m, n), tuple(lead) + (n,)):
+        raise ValueError(f"out must have shape {(m, n)} or {tuple(lead) + (n,)}, got {tuple(out.shape)}")
+    return out
+
+
+def _workspace(workspace, need: int, device):
+    """A caller's workspace, or a new one: contiguous uint8 bytes on the
+    inputs' device (its size is checked by the library)."""
+    torch = _torch()
+    if workspace is None:
+        return torch.empty((max(need, 1),), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8:
+        raise TypeError(f"workspace must be uint8, got {workspace.dtype}")
+    if workspace.device != device:
+        raise ValueError(f"workspace is on {workspace.device}, the inputs on {device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace
+
+
 def sparsify_2of4(x, fold_scale: bool = False, with_scale: bool = True):
     """Mask, compensation scale and canonical compression of x [..., K].
 
@@ -151,7 +183,6 @@ def sparsify_2of4(x, fold_scale: bool = False, with_scale: bool = True):
 def sparse_linear(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.0, out=None, workspace=None):
     """Y = S(X) W^T + lora_scale * ((X - S(X)) A^T) B^T for x [..., K], w [N, K],
     lora_a [r, K], lora_b [N, r] (bf16, device).  Returns y [..., N] bf16."""
-    torch = _torch()
     x2 = _as_2d(x, "x")
     w2 = _as_2d(w, "w")
     m, k = x2.shape
@@ -168,10 +199,8 @@ def sparse_linear(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.0, out=N
         if lora_a.shape[1] != k or lora_b.shape != (n, r):
             raise ValueError(f"LoRA shapes {tuple(lora_a.shape)}, {tuple(lora_b.shape)} do not match "
                              f"K={k}, N={n}")
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x2.device)
-    need = sparse_linear_workspace_bytes(m, k, r)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
+    y = _out(out, m, n, x.shape[:-1], x2.device)
+    workspace = _workspace(workspace, sparse_linear_workspace_bytes(m, k, r), x2.device)
     st = lib().rtl_sparse_linear(
         x2.data_ptr(), w2.data_ptr(),
         lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None,
@@ -185,7 +214,6 @@ def sparse_linear_noalloc(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.
     library's fixed per-GPU scratch array (NOALLOC_SCRATCH_BYTES) stands in
     for it, so with ``out`` given nothing is allocated.  Calls that can
     overlap on one GPU share that array and must be serialised."""
-    torch = _torch()
     x2 = _as_2d(x, "x")
     w2 = _as_2d(w, "w")
     m, k = x2.shape
@@ -202,7 +230,7 @@ def sparse_linear_noalloc(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.
         if lora_a.shape[1] != k or lora_b.shape != (n, r):
             raise ValueError(f"LoRA shapes {tuple(lora_a.shape)}, {tuple(lora_b.shape)} do not match "
                              f"K={k}, N={n}")
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x2.device)
+    y = _out(out, m, n, x.shape[:-1], x2.device)
     st = lib().rtl_sparse_linear_noalloc(
         x2.data_ptr(), w2.data_ptr(), lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None,
         m, n, k, r, float(lora_scale), y.data_ptr(), _stream())
@@ -223,7 +251,6 @@ def prepare(x, lora_a=None, lora_scale: float = 1.0, workspace=None, variant: in
     """First half of sparse_linear: reads x once (rtl_sparse_linear_prepare,
     or rtl_sparse_linear_prepare_variant for a nonzero ``variant``: one of
     COMP_* | one of LORA_*)."""
-    torch = _torch()
     x2 = _as_2d(x, "x")
     m, k = x2.shape
     r = 0
@@ -232,9 +259,7 @@ def prepare(x, lora_a=None, lora_scale: float = 1.0, workspace=None, variant: in
         r = lora_a.shape[0]
         if lora_a.shape[1] != k:
             raise ValueError(f"lora_a has {lora_a.shape[1]} input channels, x has {k}")
-    need = sparse_linear_workspace_bytes(m, k, r)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
+    workspace = _workspace(workspace, sparse_linear_workspace_bytes(m, k, r), x2.device)
     if variant:
         st = lib().rtl_sparse_linear_prepare_variant(x2.data_ptr(), lora_a.data_ptr() if r else None, m, k, r,
                                                      float(lora_scale), int(variant), workspace.data_ptr(),
@@ -249,7 +274,6 @@ def prepare(x, lora_a=None, lora_scale: float = 1.0, workspace=None, variant: in
 
 def apply(prep: Prepared, w, lora_b=None, out=None):
     """Second half of sparse_linear: sparse GEMM + scale + LoRA-up (rtl_sparse_linear_apply)."""
-    torch = _torch()
     w2 = _as_2d(w, "w")
     n = w2.shape[0]
     if w2.shape[1] != prep.k:
@@ -260,7 +284,9 @@ def apply(prep: Prepared, w, lora_b=None, out=None):
         lora_b = _as_2d(lora_b, "lora_b")
         if tuple(lora_b.shape) != (n, prep.r):
             raise ValueError(f"lora_b must be [{n}, {prep.r}], got {tuple(lora_b.shape)}")
-    y = out if out is not None else torch.empty((prep.m, n), dtype=torch.bfloat16, device=w2.device)
+    if w2.device != prep.workspace.device:
+        raise ValueError(f"w is on {w2.device}, the prepared activation on {prep.workspace.device}")
+    y = _out(out, prep.m, n, prep.lead_shape, w2.device)
     st = lib().rtl_sparse_linear_apply(prep.workspace.data_ptr(), prep.workspace.numel(), w2.data_ptr(),
                                        lora_b.data_ptr() if prep.r else None, prep.m, n, prep.k, prep.r,
                                        y.data_ptr(), _stream())
@@ -284,10 +310,8 @@ def sparse_linear_compressed(vals, idx, scale, w, out=None, workspace=None):
         raise ValueError("idx must be a contiguous uint8 device tensor [M, ceil(K/8)]")
     if scale is not None and (scale.dtype != torch.float32 or not scale.is_cuda or scale.numel() != m):
         raise ValueError("scale must be a float32 device tensor [M] or None")
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=w2.device)
-    need = sparse_linear_workspace_bytes(m, k, 0)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=w2.device)
+    y = _out(out, m, n, (m,), w2.device)
+    workspace = _workspace(workspace, sparse_linear_workspace_bytes(m, k, 0), w2.device)
     st = lib().rtl_sparse_linear_compressed(v2.data_ptr(), idx.data_ptr(),
                                             scale.data_ptr() if scale is not None else None,
                                             w2.data_ptr(), m, n, k, y.data_ptr(), workspace.data_ptr(),
@@ -298,14 +322,13 @@ def sparse_linear_compressed(vals, idx, scale, w, out=None, workspace=None):
 
 def dense_linear(x, w, out=None):
     """Y = X W^T on the dense matrix cores (the baseline)."""
-    torch = _torch()
     x2 = _as_2d(x, "x")
     w2 = _as_2d(w, "w")
     m, k = x2.shape
     n = w2.shape[0]
     if w2.shape[1] != k:
         raise ValueError(f"w has {w2.shape[1]} input channels, x has {k}")
-    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x2.device)
+    y = _out(out, m, n, x.shape[:-1], x2.device)
     st = lib().rtl_dense_linear(x2.data_ptr(), w2.data_ptr(), m, n, k, y.data_ptr(), _stream())
     _check(st, "rtl_dense_linear")
     return y.reshape(*x.shape[:-1], n)

@@ -14,7 +14,7 @@ from __future__ import annotations
 
 import ctypes
 
-from . import _as_2d, _check, _stream, lib, sparse_linear_workspace_bytes
+from . import _as_2d, _check, _out, _stream, _workspace, lib, sparse_linear_workspace_bytes
 
 DENSE = 0x100
 
@@ -56,7 +56,6 @@ class LayerPolicy:
                workspace=None):
         """Layer ``layer`` on x [..., K] with weight w [N, K] and LoRA factors
         (used by sparse layers only).  Returns y [..., N] bf16."""
-        import torch
         x2 = _as_2d(x, "x")
         w2 = _as_2d(w, "w")
         m, k = x2.shape
@@ -73,10 +72,9 @@ class LayerPolicy:
             if lora_a.shape[1] != k or tuple(lora_b.shape) != (n, r):
                 raise ValueError(f"LoRA shapes {tuple(lora_a.shape)}, {tuple(lora_b.shape)} do not match "
                                  f"K={k}, N={n}")
-        y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=x2.device)
-        if workspace is None and self.mode(layer) != DENSE:
-            need = sparse_linear_workspace_bytes(m, k, r)
-            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
+        y = _out(out, m, n, x.shape[:-1], x2.device)
+        if self.mode(layer) != DENSE:
+            workspace = _workspace(workspace, sparse_linear_workspace_bytes(m, k, r), x2.device)
         st = _fn()(self.modes, self.num_layers, layer, x2.data_ptr(), w2.data_ptr(),
                    lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None, m, n, k, r,
                    float(lora_scale), y.data_ptr(), workspace.data_ptr() if workspace is not None else None,

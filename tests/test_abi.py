@@ -197,6 +197,34 @@ def test_noalloc_limit_is_the_workspace_size():
         assert _na(r=0, a=None, b=None) == NODEV
 
 
+def test_output_and_workspace_checks():
+    """A caller's out= must be exactly the bf16 [M, N] (or [..., N]) block the
+    kernels write, on the inputs' device; a caller's workspace contiguous
+    uint8 bytes on that device."""
+    import torch
+    cpu = torch.device("cpu")
+    good = torch.zeros(6, 8, dtype=torch.bfloat16)
+    assert rtl._out(good, 6, 8, (6,), cpu) is good
+    assert rtl._out(torch.zeros(2, 3, 8, dtype=torch.bfloat16), 6, 8, (2, 3), cpu).shape == (2, 3, 8)
+    assert rtl._out(None, 6, 8, (6,), cpu).shape == (6, 8)
+    for bad, exc in [(torch.zeros(6, 8, dtype=torch.float32), TypeError),
+                     (torch.zeros(5, 8, dtype=torch.bfloat16), ValueError),
+                     (torch.zeros(6, 9, dtype=torch.bfloat16), ValueError),
+                     (torch.zeros(48, dtype=torch.bfloat16), ValueError),
+                     (torch.zeros(8, 6, dtype=torch.bfloat16).t(), ValueError),
+                     (torch.zeros(6, 8, dtype=torch.bfloat16, device="meta"), ValueError)]:
+        with pytest.raises(exc):
+            rtl._out(bad, 6, 8, (6,), cpu)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    assert rtl._workspace(ws, 512, cpu) is ws
+    assert rtl._workspace(None, 512, cpu).numel() == 512
+    for bad, exc in [(torch.zeros(256, dtype=torch.float32), TypeError),
+                     (torch.zeros(1024, dtype=torch.uint8, device="meta"), ValueError),
+                     (torch.zeros(2048, dtype=torch.uint8)[::2], ValueError)]:
+        with pytest.raises(exc):
+            rtl._workspace(bad, 512, cpu)
+
+
 def _pr(x=P, a=P2, m=64, k=256, r=8, alpha=1.0, ws=WSP, wsb=BIG, stream=None):
     return rtl.lib().rtl_sparse_linear_prepare(x, a, m, k, r, alpha, ws, wsb, stream)
 

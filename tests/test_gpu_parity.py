@@ -266,6 +266,33 @@ def test_subnormal_and_large_magnitude_inputs():
         assert_y_close(y[big], ref[big], f"rows near 1e34 K={k}")
 
 
+def test_wrappers_reject_bad_out_and_workspace():
+    """An output or workspace the kernels could not write safely is refused
+    before any launch, and the valid call afterwards is unaffected."""
+    rng = np.random.default_rng(3)
+    x = to_dev(gen.mixture_bernoulli(rng, 64, 256))
+    w = to_dev(gen.gaussian_bits(rng, (96, 256), 0.02))
+    bad_outs = [torch.empty((64, 95), dtype=torch.bfloat16, device=DEV),
+                torch.empty((64, 96), dtype=torch.float32, device=DEV),
+                torch.empty((96, 64), dtype=torch.bfloat16, device=DEV).t(),
+                torch.empty((64, 96), dtype=torch.bfloat16)]
+    for o in bad_outs:
+        with pytest.raises((TypeError, ValueError)):
+            rtl.sparse_linear(x, w, out=o)
+        with pytest.raises((TypeError, ValueError)):
+            rtl.dense_linear(x, w, out=o)
+    need = rtl.sparse_linear_workspace_bytes(64, 256, 0)
+    for ws in [torch.empty((need,), dtype=torch.float32, device=DEV),
+               torch.empty((need,), dtype=torch.uint8)]:
+        with pytest.raises((TypeError, ValueError)):
+            rtl.sparse_linear(x, w, workspace=ws)
+    y = torch.empty((64, 96), dtype=torch.bfloat16, device=DEV)
+    rtl.sparse_linear(x, w, out=y)
+    torch.cuda.synchronize()
+    xh = to_host(x)
+    assert_y_close(y_to_f64(y), oracle.sparse_linear_ref(xh, to_host(w)), "after rejected calls")
+
+
 def test_bitwise_repeatable():
     x, w, a, b = gen.make_config("attn_proj", m=512)
     y1 = to_host(run_sparse_linear(x, w, a, b))
