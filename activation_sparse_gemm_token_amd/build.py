@@ -18,6 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librtlynx.so")
+# The matrix-instruction rate measurement (bench.py --mfma-rates): not part
+# of librtlynx, built beside it.
+MB_SRC = os.path.join(PKG, "microbench", "mfma_rates.hip")
+MB_LIB = os.path.join(PKG, "libmfma_rates.so")
 
 ARCH = "gfx950"
 COMMON = [
@@ -70,8 +74,15 @@ def build(verbose: bool = True) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{res.stderr}")
     os.replace(tmp, LIB)
+    mb_obj = _compile(MB_SRC)
+    tmp = MB_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, mb_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{res.stderr}")
+    os.replace(tmp, MB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {MB_LIB}")
     return LIB
 
 
