@@ -220,23 +220,6 @@ class ClockSampler:
                 "readings": len(s)}
 
 
-def sclk_by_spin(stream, cycles: int = 1 << 20):
-    """The shader clock in MHz, measured on the GPU: torch's spin kernel
-    waits until the shader-clock counter (s_memtime) has advanced by
-    `cycles`, and events time it on `stream`.  Queued right after the timed
-    loop (outside it), it reads the clock the loop ended at (the driver's
-    own metrics refresh too slowly for a loop of a few ms; a spin queued
-    after the idle gap of a synchronize reads the clock that gap let fall).
-    Returns a lazy value (the events are read after the next sync)."""
-    import torch
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    torch.cuda._sleep(cycles)
-    e1.record(stream)
-    return lambda: round(cycles / (e0.elapsed_time(e1) * 1e-3) / 1e6, 1)
-
-
 def dist(ms_list):
     """median / min / p90 / mean of per-launch times, in microseconds."""
     v = sorted(ms_list)
@@ -289,9 +272,14 @@ def run_suite(reps: int, warmup: int):
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ws = torch.empty((rtl.sparse_linear_workspace_bytes(m, k, r),), dtype=torch.uint8, device=dev)
         t_layer = mean_ms(lambda: rtl.sparse_linear(xd, wd, ad, bd, 1.0, out=y, workspace=ws))
-        t_prep = mean_ms(lambda: rtl.prepare(xd, ad, 1.0, workspace=ws))
+        # the halves through the C entry points, arguments marshalled once
+        # (a 13 us pre-pass is shorter than a wrapped call's host time)
+        clib, sp = rtl.lib(), stream.cuda_stream
+        prep_args = (xd.data_ptr(), ad.data_ptr(), m, k, r, 1.0, ws.data_ptr(), ws.numel(), sp)
+        apply_args = (ws.data_ptr(), ws.numel(), wd.data_ptr(), bd.data_ptr(), m, n, k, r, y.data_ptr(), sp)
+        t_prep = mean_ms(lambda: clib.rtl_sparse_linear_prepare(*prep_args))
         prep = rtl.prepare(xd, ad, 1.0, workspace=ws)
-        t_apply = mean_ms(lambda: rtl.apply(prep, wd, bd, out=y))
+        t_apply = mean_ms(lambda: clib.rtl_sparse_linear_apply(*apply_args))
         t_dense = mean_ms(lambda: rtl.dense_linear(xd, wd, out=y))
         wt = wd.t()
         t_blas = mean_ms(lambda: torch.matmul(xd, wt, out=y))
@@ -421,6 +409,78 @@ def run_variants(reps: int, warmup: int):
                               "dev_vs_dense": round(rel_dev(y, yd), 5)}), flush=True)
 
 
+MFMA_KINDS = (
+    # kind, instruction, dense-equivalent flops, nominal cycles per SIMD at
+    # the dense peak (2048 dense MACs per CU per clock; the structured-sparse
+    # instructions at twice the dense-equivalent rate)
+    (0, "v_mfma_f32_16x16x32_bf16", 2 * 16 * 16 * 32, 16),
+    (1, "v_mfma_f32_32x32x16_bf16", 2 * 32 * 32 * 16, 32),
+    (2, "v_smfmac_f32_16x16x64_bf16", 2 * 16 * 16 * 64, 16),
+    (3, "v_smfmac_f32_32x32x32_bf16", 2 * 32 * 32 * 32, 32),
+)
+
+
+def run_mfma_rates(iters: int = 2048):
+    """Issue rate of the bf16 matrix instructions (microbench/mfma_rates.hip):
+    one line per instruction and wavefronts per SIMD, with the cycles per
+    instruction per SIMD from the shader clock, the dense-equivalent TFLOP/s
+    from events, the clock, and the fraction of the nominal rate."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "activation_sparse_gemm_token_amd", "libmfma_rates.so")
+    mb = ctypes.CDLL(path)
+    fn = mb.mb_mfma_rate
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    dev = "cuda:0"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    for kind, name, flops, nominal in MFMA_KINDS:
+        for waves in (4, 8):
+            blocks = cus
+            cyc = torch.zeros((blocks * waves,), dtype=torch.int64, device=dev)
+            sink = torch.zeros((blocks * 64 * waves,), dtype=torch.float32, device=dev)
+
+            def launch():
+                st = fn(kind, blocks, waves, iters, cyc.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+                if st != 0:
+                    raise RuntimeError(f"mb_mfma_rate launch failed: {st}")
+
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < RAMP_MS * 1e-3:
+                launch()
+                torch.cuda.synchronize()
+            times, cycles = [], []
+            for _ in range(5):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e-3)
+                # the longest loop of each CU: with two wavefronts per SIMD
+                # they share the matrix core unevenly, the last to finish
+                # spans the whole issue
+                per_cu = cyc.view(blocks, waves).max(dim=1).values
+                cycles.append(statistics.median(per_cu.cpu().tolist()))
+            t = statistics.median(times)
+            c = statistics.median(cycles)
+            per_simd = waves // 4
+            instr = blocks * waves * iters * 8
+            cpi = c / (iters * 8 * per_simd)
+            tflops = instr * flops / t / 1e12
+            mhz = c / t / 1e6
+            print(json.dumps({"instruction": name, "wavefronts_per_simd": per_simd,
+                              "cycles_per_instruction_per_simd": round(cpi, 2), "nominal_cycles": nominal,
+                              "frac_of_nominal_rate": round(nominal / cpi, 4),
+                              "dense_equivalent_tflops": round(tflops, 1), "shader_clock_mhz": round(mhz, 1),
+                              "cus": cus, "iters": iters}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -439,6 +499,8 @@ def main():
                          "output folders of --counters runs (FETCH_SIZE, WRITE_SIZE) and exit")
     ap.add_argument("--variants", action="store_true",
                     help="deviation from the dense product and time of every compensation / LoRA-input variant")
+    ap.add_argument("--mfma-rates", action="store_true",
+                    help="issue rate of the bf16 dense and structured-sparse matrix instructions; one JSON line each")
     ap.add_argument("--suite", action="store_true",
                     help="time every linear-layer workload and one DiT block's linears; one JSON line each")
     args = ap.parse_args()
@@ -456,6 +518,9 @@ def main():
         sys.exit(2)
     if args.suite:
         run_suite(args.steps, args.warmup)
+        return
+    if args.mfma_rates:
+        run_mfma_rates()
         return
     if args.variants:
         run_variants(min(args.steps, 100), min(args.warmup, 100))
@@ -527,7 +592,6 @@ def main():
     for _ in range(args.steps):
         step()
     t_end.record(stream)
-    sclk_after = sclk_by_spin(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
@@ -544,8 +608,29 @@ def main():
     prep_ms = [e[0].elapsed_time(e[1]) for e in ev]
     apply_ms = [e[1].elapsed_time(e[2]) for e in ev]
     step_ms = [e[0].elapsed_time(e[2]) for e in ev]
-    prep_avg = sum(prep_ms) / len(prep_ms)
-    apply_avg = sum(apply_ms) / len(apply_ms)
+
+    # Average launch duration of each half: K back-to-back launches of it
+    # between two events (an event between every launch inflates a 13 us
+    # kernel by several us), issued through the C entry points with their
+    # arguments marshalled once, so that the host keeps ahead of a 13 us
+    # kernel.
+    def block_ms(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    clib = rtl.lib()
+    sp = stream.cuda_stream
+    prep_args = (xd.data_ptr(), ad.data_ptr(), m, k, r, 1.0, ws.data_ptr(), ws.numel(), sp)
+    apply_args = (ws.data_ptr(), ws.numel(), wd.data_ptr(), bd.data_ptr(), m, n, k, r, y.data_ptr(), sp)
+    prep_avg = block_ms(lambda: clib.rtl_sparse_linear_prepare(*prep_args))
+    clib.rtl_sparse_linear_prepare(*prep_args)
+    apply_avg = block_ms(lambda: clib.rtl_sparse_linear_apply(*apply_args))
 
     flops_dense_eq = 2.0 * m * n * k
     value = flops_dense_eq / (ms_step * 1e-3) / 1e12
@@ -657,8 +742,10 @@ def main():
     del flush
 
     # Graphics clock under this load, read from the driver while ~1 s of
-    # steps runs; the peaks rescaled to it say how much of the gap to the
-    # nominal 2.4 GHz peak is the clock.
+    # steps runs (its metrics lag by a few hundred ms: a loop of a few ms is
+    # too short for them, and a clock read on the GPU right after the loop
+    # sees the clock rise as the load drops); the peaks rescaled to it say
+    # how much of the gap to the nominal 2.4 GHz peak is the clock.
     for _ in range(200):
         step()
     torch.cuda.synchronize()
@@ -669,10 +756,7 @@ def main():
     h3 = time.perf_counter()
     clk.stop()
     sclk_obs = clk.window(h2, h3)
-    # the clock the timed loop ended at, from the GPU's own counter; the
-    # driver's reading as a fallback
-    sclk_spin = sclk_after()
-    sclk = sclk_spin if sclk_spin and 500.0 < sclk_spin < 3000.0 else (sclk_obs["median"] if sclk_obs else None)
+    sclk = sclk_obs["median"] if sclk_obs else None
     log(f"[bench] cold step {cold_step['median']} us, dense {cold_dense['median']} us; sclk {sclk_obs} MHz")
 
     # Roofline of the dominant kernel: the structured-sparse GEMM (apply).
@@ -750,7 +834,6 @@ def main():
             "wcold_hipblaslt_us": wcold_blas,
             "wcold_speedup_vs_inhouse_dense": round(wcold_dense["median"] / wcold_step["median"], 3),
             "wcold_speedup_vs_hipblaslt": round(wcold_blas["median"] / wcold_step["median"], 3),
-            "sclk_mhz_after_timed_loop": sclk_spin,
             "sclk_mhz_observed": sclk_obs,
             "frac_dense_peak_at_sclk": round(value / peak_at_sclk, 4) if sclk else None,
             "apply_frac_peak_at_sclk": round(achieved / peak_at_sclk, 4) if sclk else None,
