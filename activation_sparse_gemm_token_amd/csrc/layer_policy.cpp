@@ -7,6 +7,14 @@
 
 #define RTL_API extern "C" __attribute__((visibility("default")))
 
+namespace rtl {
+// rtl_sparse_linear_apply with the choice of the GEMM instance that probes
+// the weights into L2 ahead of their copies (rtlynx_api.cpp).
+rtl_status apply_impl(const void* workspace, size_t workspace_bytes, const uint16_t* w, const uint16_t* lora_b,
+                      int64_t M, int64_t N, int64_t K, int64_t r, uint16_t* y, void* hip_stream,
+                      bool prefetch_w);
+}  // namespace rtl
+
 namespace {
 
 // A sparsification variant as rtl_sparse_linear_prepare_variant accepts it:
@@ -31,14 +39,16 @@ RTL_API rtl_status rtl_layer_linear(const uint32_t* layer_modes, int64_t num_lay
                                     void* hip_stream) {
   if (num_layers < 0 || layer < 0 || layer >= num_layers) return RTL_ERR_BAD_SHAPE;
   if (layer_modes == nullptr) return RTL_ERR_NULL_POINTER;
-  const uint32_t mode = layer_modes[layer];
+  const uint32_t mode = layer_modes[layer] & ~RTL_LAYER_STREAM_W;
+  const bool stream_w = (layer_modes[layer] & RTL_LAYER_STREAM_W) != 0;
   if (mode == RTL_LAYER_DENSE) return rtl_dense_linear(x, w, M, N, K, y, hip_stream);
   if (!valid_variant(mode)) return RTL_ERR_BAD_FLAGS;
-  if (mode == 0)
+  if (mode == 0 && !stream_w)
     return rtl_sparse_linear(x, w, lora_a, lora_b, M, N, K, r, lora_scale, y, workspace, workspace_bytes,
                              hip_stream);
-  // A variant: prepare, then apply.  Every argument of the apply is checked
-  // before the prepare runs, so an invalid call launches nothing.
+  // A variant, or weights streamed: prepare, then apply.  Every argument of
+  // the apply is checked before the prepare runs, so an invalid call
+  // launches nothing.
   if (N < 0 || !apply_sizes_ok(M, N, K, r)) return RTL_ERR_BAD_SHAPE;
   if (M > 0 && N > 0 && (w == nullptr || y == nullptr || (r > 0 && lora_b == nullptr)))
     return RTL_ERR_NULL_POINTER;
@@ -51,5 +61,5 @@ RTL_API rtl_status rtl_layer_linear(const uint32_t* layer_modes, int64_t num_lay
   rtl_status st = rtl_sparse_linear_prepare_variant(x, lora_a, M, K, r, lora_scale, mode, workspace,
                                                     workspace_bytes, hip_stream);
   if (st != RTL_OK) return st;
-  return rtl_sparse_linear_apply(workspace, workspace_bytes, w, lora_b, M, N, K, r, y, hip_stream);
+  return rtl::apply_impl(workspace, workspace_bytes, w, lora_b, M, N, K, r, y, hip_stream, stream_w);
 }

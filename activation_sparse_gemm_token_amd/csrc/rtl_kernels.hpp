@@ -21,9 +21,13 @@ hipError_t launch_prepass(const uint16_t* x, const uint16_t* lora_a, int64_t M, 
 // `compute_units`: the device's CU count (the persistent grid's size).
 // tile_n: 256 or 192 output columns per tile, 0 to let
 // sparse_gemm_tile_n choose (the one that fills the CUs at lower cost).
+// prefetch_w: probe W lines into L2 a few steps ahead of their copies (for
+// weights not expected in the caches; the ring shapes, r % 8 == 0 and
+// K % 8 == 0, only).
 hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const uint16_t* lora_b,
                               int64_t M, int64_t N, int64_t K, int64_t r, uint16_t* y,
-                              int compute_units, hipStream_t stream, int tile_n = 0);
+                              int compute_units, hipStream_t stream, int tile_n = 0,
+                              bool prefetch_w = false);
 int sparse_gemm_tile_n(int64_t M, int64_t N, int64_t K, int compute_units);
 
 hipError_t launch_dense_gemm(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N,

@@ -169,10 +169,11 @@ RTL_API rtl_status rtl_sparse_linear_prepare_variant(const uint16_t* x, const ui
                                       static_cast<hipStream_t>(hip_stream), (int)comp, (int)lora));
 }
 
-RTL_API rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspace_bytes,
-                                           const uint16_t* w, const uint16_t* lora_b, int64_t M,
-                                           int64_t N, int64_t K, int64_t r, uint16_t* y,
-                                           void* hip_stream) {
+namespace rtl {
+
+rtl_status apply_impl(const void* workspace, size_t workspace_bytes, const uint16_t* w, const uint16_t* lora_b,
+                      int64_t M, int64_t N, int64_t K, int64_t r, uint16_t* y, void* hip_stream,
+                      bool prefetch_w) {
   if (!dims_ok(M, K) || N < 0 || N >= kMaxDim || r < 0 || r > RTL_MAX_LORA_RANK) return RTL_ERR_BAD_SHAPE;
   if (!layer_sizes_ok(M, N, K, r)) return RTL_ERR_BAD_SHAPE;
   if (M == 0 || N == 0) return RTL_OK;
@@ -185,7 +186,16 @@ RTL_API rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspa
   const rtl_status d = check_device(&cus);
   if (d != RTL_OK) return d;
   return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y, cus,
-                                          static_cast<hipStream_t>(hip_stream)));
+                                          static_cast<hipStream_t>(hip_stream), 0, prefetch_w));
+}
+
+}  // namespace rtl
+
+RTL_API rtl_status rtl_sparse_linear_apply(const void* workspace, size_t workspace_bytes,
+                                           const uint16_t* w, const uint16_t* lora_b, int64_t M,
+                                           int64_t N, int64_t K, int64_t r, uint16_t* y,
+                                           void* hip_stream) {
+  return rtl::apply_impl(workspace, workspace_bytes, w, lora_b, M, N, K, r, y, hip_stream, false);
 }
 
 RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const uint16_t* lora_a,

@@ -56,7 +56,8 @@ struct Tile {
   static constexpr int kLoraBytes = kLoraBOff + 4 * CB * 1024;
   static constexpr int kStageBytes = kKStepBytes > kLoraBytes ? kKStepBytes : kLoraBytes;
   static constexpr int kScaleOff = kStages * kStageBytes;
-  static constexpr int kLdsBytes = kScaleOff + 2048;
+  static constexpr int kProbeOff = kScaleOff + 2048;          // 8 x 256 B, L2 prefetch probes
+  static constexpr int kLdsBytes = kProbeOff + 2048;
   // Vector-memory operations every step issues per wavefront: CB for the W
   // tile, 2 for the A fragments, 1 for the position fields (a LoRA step
   // pads to the same count, so the vmcnt waits are uniform).
@@ -269,6 +270,24 @@ __device__ __forceinline__ void dma_lora_tile_asm(__amdgpu_buffer_rsrc_t tr, __a
   (void)saved;
 }
 
+// L2 prefetch probe: one dword per lane by DMA into a throwaway LDS area
+// (no register is written, so nothing waits for it); lanes given
+// kOobOffset touch no memory.  One vector-memory operation.
+__device__ __forceinline__ void l2_probe_asm(__amdgpu_buffer_rsrc_t wr, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[l]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %[v], %[rs], 0 offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [v] "v"(voff), [rs] "s"(wr), [l] "s"(lds_addr)
+      : "memory");
+  (void)saved;
+}
+
 // Copies the workgroup's 256 per-token scales into LDS: wavefronts 0-3 move
 // 64 each with one dword DMA.  (The other wavefronts issue nothing; the
 // vmcnt waits after it only bound later operations, so they hold for both.)
@@ -301,7 +320,17 @@ __device__ __forceinline__ void dma_scale_asm(__amdgpu_buffer_rsrc_t sr, uint32_
 // RING: the LoRA-up runs as extra steps of the LDS ring (r % 8 == 0 and
 // 16-byte W rows).  Otherwise it runs in the epilogue from global memory
 // (odd ranks, K % 8 == 4: shapes outside the fast path).
-template <int KM, bool RING, int CB>
+//
+// PFW (weights expected cold, only with RING): every k-step one wavefront
+// in turn probes 32 rows of the W slice kPfDist steps past the one being
+// copied, one dword per 128-byte line, so that the line is on its way from
+// HBM into L2 when its copy is issued; the 8 workgroups of an XCD that
+// share a W slice (an 8 x 4 block of tiles, tile_coords_of) probe its 256
+// rows between them, by tile row.  A tile's first kPfDist steps are not
+// probed.  The probes' completion is never awaited: the issuing
+// wavefront's vmcnt waits then also cover them, which only makes those
+// waits stricter.
+template <int KM, bool RING, int CB, bool PFW>
 __global__ void __launch_bounds__(kThreads, 1)
 sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi,
                    const float* __restrict__ s, const u32x4* __restrict__ tfrag,
@@ -309,6 +338,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
                    int64_t M, int64_t N, int64_t K, int64_t r, int64_t kpairs,
                    int64_t rsteps, uint16_t* __restrict__ y) {
   static_assert(!RING || KM != kAligned8, "the ring's uniform waits need CB + 3 operations per step");
+  static_assert(RING || !PFW, "W probes come with the ring");
   static_assert(CB == 4 || KM != kAligned8, "the dword tile copy moves 256 rows");
   using T = Tile<CB>;
   constexpr int kCB = CB, kWaveN = T::kWaveN, kTileN = T::kTileNc;
@@ -360,11 +390,13 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   // there: the extra copies are harmless repeats into free stages.
   int pc_i = 0, pc_loc = 0;
   int64_t pc_n0 = 0;
+  uint32_t pf_r0 = 0;   // PFW: the first of the 32 W rows this workgroup probes in the cursor's tile
   uint32_t pc_tb0 = 0, pc_wso = 0, pc_aso = 0, pc_iso = 0, pc_wv = 0;
   auto cursor_tile = [&](int i) {
     int64_t tm, tn;
     tile_coords_of((int64_t)blockIdx.x + (int64_t)i * G, tiles_m, tiles_n, tm, tn);
     pc_n0 = tn * kTileN;
+    if constexpr (PFW) pf_r0 = __builtin_amdgcn_readfirstlane((uint32_t)(pc_n0 + 32 * (tm & 7)));
     pc_aso = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 8192) + a_wave);
     pc_iso = __builtin_amdgcn_readfirstlane((uint32_t)(2 * tm * ksteps * 1024) + i_wave);
     pc_tb0 = __builtin_amdgcn_readfirstlane((uint32_t)(tm * 16 * rsteps * 2048));
@@ -393,6 +425,17 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
       }
     } else {
       if constexpr (RING) dma_lora_tile_asm<kCB, kOps>(tr, br, pc_tb0, rsteps, pc_loc - ksteps, N, r, pc_n0, st);
+    }
+    if constexpr (PFW) {
+      constexpr int kPfDist = 4;
+      const int tgt = pc_loc + kPfDist;
+      if (((pc_loc + pc_i) & 7) == wave && tgt < ksteps) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(pf_r0 * (uint32_t)(2 * K) + (uint32_t)tgt * (2u * kTileK));
+        const int64_t left = N - (int64_t)pf_r0;
+        const uint32_t lim = left < 32 ? (uint32_t)(left > 0 ? left : 0) : 32u;
+        const uint32_t voff = (uint32_t)lane < lim ? base + (uint32_t)lane * (uint32_t)(2 * K) : kOobOffset;
+        l2_probe_asm(wr, voff, lds_base + (uint32_t)T::kProbeOff + 256u * (uint32_t)wave);
+      }
     }
     if (pc_loc + 1 < spt) {
       ++pc_loc;
@@ -670,18 +713,22 @@ template <int CB>
 hipError_t launch_sparse_gemm_t(const u32x4* xv, const uint16_t* xi, const float* s, const u32x4* t,
                                 const uint16_t* w, const uint16_t* lora_b, int64_t M, int64_t N, int64_t K,
                                 int64_t r, int64_t kpairs, int64_t rsteps, uint16_t* y, int64_t cus,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool prefetch_w) {
   const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + Tile<CB>::kTileNc - 1) / Tile<CB>::kTileNc);
   // One persistent workgroup per CU (the LDS allows one), at most one per tile.
   const dim3 grid((unsigned)(tiles < cus ? tiles : cus)), block(kThreads);
   // The k loop runs over the padded K (a multiple of 128): full-K mode
   // needs K itself to be one.
   const bool ring = r % 8 == 0;
-  using Kern = decltype(&sparse_gemm_kernel<kFullK, true, CB>);
+  using Kern = decltype(&sparse_gemm_kernel<kFullK, true, CB, false>);
   Kern k = nullptr;
-  if (K % 128 == 0) k = ring ? &sparse_gemm_kernel<kFullK, true, CB> : &sparse_gemm_kernel<kFullK, false, CB>;
-  else if (K % 8 == 0) k = ring ? &sparse_gemm_kernel<kAligned16, true, CB> : &sparse_gemm_kernel<kAligned16, false, CB>;
-  else if constexpr (CB == 4) k = &sparse_gemm_kernel<kAligned8, false, CB>;
+  if (K % 128 == 0)
+    k = !ring ? &sparse_gemm_kernel<kFullK, false, CB, false>
+        : prefetch_w ? &sparse_gemm_kernel<kFullK, true, CB, true> : &sparse_gemm_kernel<kFullK, true, CB, false>;
+  else if (K % 8 == 0)
+    k = !ring ? &sparse_gemm_kernel<kAligned16, false, CB, false>
+        : prefetch_w ? &sparse_gemm_kernel<kAligned16, true, CB, true> : &sparse_gemm_kernel<kAligned16, true, CB, false>;
+  else if constexpr (CB == 4) k = &sparse_gemm_kernel<kAligned8, false, CB, false>;
   if (k == nullptr) return hipErrorInvalidValue;   // K % 8 == 4 takes 256-column tiles
   return launch(k, grid, block, stream, xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y);
 }
@@ -701,7 +748,7 @@ int sparse_gemm_tile_n(int64_t M, int64_t N, int64_t K, int compute_units) {
 
 hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const uint16_t* lora_b,
                               int64_t M, int64_t N, int64_t K, int64_t r, uint16_t* y,
-                              int compute_units, hipStream_t stream, int tile_n) {
+                              int compute_units, hipStream_t stream, int tile_n, bool prefetch_w) {
   const WsLayout L = ws_layout(M, K, r);
   const char* ws = static_cast<const char*>(workspace);
   const u32x4* xv = reinterpret_cast<const u32x4*>(ws + L.off_xv);
@@ -712,8 +759,8 @@ hipError_t launch_sparse_gemm(const void* workspace, const uint16_t* w, const ui
   const int64_t cus = compute_units > 0 ? compute_units : 1;
   if (tile_n == 0) tile_n = sparse_gemm_tile_n(M, N, K, compute_units);
   if (tile_n == 192 && K % 8 == 0)
-    return launch_sparse_gemm_t<3>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y, cus, stream);
-  return launch_sparse_gemm_t<4>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y, cus, stream);
+    return launch_sparse_gemm_t<3>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y, cus, stream, prefetch_w);
+  return launch_sparse_gemm_t<4>(xv, xi, s, t, w, lora_b, M, N, K, r, kpairs, rsteps, y, cus, stream, prefetch_w);
 }
 
 }  // namespace rtl

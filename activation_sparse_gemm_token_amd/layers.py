@@ -8,7 +8,11 @@ article, section 03, item 3).  A ``LayerPolicy`` holds one mode per layer --
 without sparsification, the LoRA branch then having no residual to act on) or
 a sparsification variant (``COMP_* | LORA_*``; 0 is the default layer) -- and
 ``policy.linear(layer, ...)`` runs one layer through the C dispatch.
-Argument marshalling only, as in the package's other bindings.
+``STREAM_W`` OR-ed into a sparse layer's mode marks its weights as not
+expected in the caches (each layer of a model running once per forward
+pass): its GEMM then probes the weight lines into L2 ahead of their copies,
+with the same output bits.  Argument marshalling only, as in the package's
+other bindings.
 """
 from __future__ import annotations
 
@@ -17,6 +21,7 @@ import ctypes
 from . import _as_2d, _check, _out, _stream, _workspace, lib, sparse_linear_workspace_bytes
 
 DENSE = 0x100
+STREAM_W = 0x200
 
 _c_i64, _c_vp = ctypes.c_int64, ctypes.c_void_p
 _SIG = (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp,
@@ -32,9 +37,10 @@ def _fn():
 class LayerPolicy:
     """Per-layer modes of a model with ``num_layers`` sparsifiable linear
     layers: every layer sparse (variant 0) unless listed in ``dense`` or
-    given a variant in ``variants``."""
+    given a variant in ``variants``; ``stream_weights`` (True for every
+    layer, or an iterable of layers) adds the ``STREAM_W`` hint."""
 
-    def __init__(self, num_layers: int, dense=(), variants=None):
+    def __init__(self, num_layers: int, dense=(), variants=None, stream_weights=()):
         if num_layers < 0:
             raise ValueError("num_layers must be >= 0")
         self.modes = (ctypes.c_uint32 * max(num_layers, 1))()
@@ -43,6 +49,10 @@ class LayerPolicy:
             self.modes[self._index(layer)] = int(v)
         for layer in dense:
             self.modes[self._index(layer)] = DENSE
+        if stream_weights is True:
+            stream_weights = range(num_layers)
+        for layer in stream_weights or ():
+            self.modes[self._index(layer)] |= STREAM_W
 
     def _index(self, layer: int) -> int:
         if not 0 <= layer < self.num_layers:
@@ -73,7 +83,7 @@ class LayerPolicy:
                 raise ValueError(f"LoRA shapes {tuple(lora_a.shape)}, {tuple(lora_b.shape)} do not match "
                                  f"K={k}, N={n}")
         y = _out(out, m, n, x.shape[:-1], x2.device)
-        if self.mode(layer) != DENSE:
+        if self.mode(layer) & ~STREAM_W != DENSE:
             workspace = _workspace(workspace, sparse_linear_workspace_bytes(m, k, r), x2.device)
         st = _fn()(self.modes, self.num_layers, layer, x2.data_ptr(), w2.data_ptr(),
                    lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None, m, n, k, r,

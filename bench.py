@@ -651,6 +651,24 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    # The same layer through the layer policy with the streamed-weights hint
+    # (the GEMM instance that probes W into L2 ahead of its copies), warm
+    # here and cold below: the trade it makes.  Both legs through the C
+    # entry points, the clock still ramped.
+    from activation_sparse_gemm_token_amd import layers as rtl_layers
+    streamed = rtl_layers.LayerPolicy(1, stream_weights=True)
+    ll = rtl_layers._fn()
+    ll_args = (streamed.modes, 1, 0, xd.data_ptr(), wd.data_ptr(), ad.data_ptr(), bd.data_ptr(), m, n, k, r, 1.0,
+               y.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    plain_args = (xd.data_ptr(), wd.data_ptr(), ad.data_ptr(), bd.data_ptr(), m, n, k, r, 1.0, y.data_ptr(),
+                  ws.data_ptr(), ws.numel(), stream.cuda_stream)
+
+    def step_stream_w():
+        ll(*ll_args)
+
+    warm_plain_ms = block_ms(lambda: clib.rtl_sparse_linear(*plain_args))
+    warm_stream_w_ms = block_ms(step_stream_w)
+
     # The same layer without the LoRA branch (r = 0): the bare sparse GEMM
     # path (pre-pass without LoRA-down, GEMM without LoRA-up).
     r0_ms = time_fn(lambda: rtl.sparse_linear(xd, wd, None, None, 1.0, out=y, workspace=ws), args.steps)
@@ -737,6 +755,8 @@ def main():
     cold_dense = time_cold(lambda: rtl.dense_linear(xd, wd, out=yd))
     cold_blas = time_cold(lambda: torch.matmul(xd, wt, out=yd))
     wcold_step = time_cold(step, warm_x=True)
+    cold_stream_w = time_cold(step_stream_w)
+    wcold_stream_w = time_cold(step_stream_w, warm_x=True)
     wcold_dense = time_cold(lambda: rtl.dense_linear(xd, wd, out=yd), warm_x=True)
     wcold_blas = time_cold(lambda: torch.matmul(xd, wt, out=yd), warm_x=True)
     del flush
@@ -834,6 +854,12 @@ def main():
             "wcold_hipblaslt_us": wcold_blas,
             "wcold_speedup_vs_inhouse_dense": round(wcold_dense["median"] / wcold_step["median"], 3),
             "wcold_speedup_vs_hipblaslt": round(wcold_blas["median"] / wcold_step["median"], 3),
+            "stream_w_cold_step_us": cold_stream_w,
+            "stream_w_wcold_step_us": wcold_stream_w,
+            "stream_w_warm_step_us": round(warm_stream_w_ms * 1e3, 2),
+            "plain_warm_step_us_c": round(warm_plain_ms * 1e3, 2),
+            "stream_w_cold_speedup_vs_hipblaslt": round(cold_blas["median"] / cold_stream_w["median"], 3),
+            "stream_w_wcold_speedup_vs_hipblaslt": round(wcold_blas["median"] / wcold_stream_w["median"], 3),
             "sclk_mhz_observed": sclk_obs,
             "frac_dense_peak_at_sclk": round(value / peak_at_sclk, 4) if sclk else None,
             "apply_frac_peak_at_sclk": round(achieved / peak_at_sclk, 4) if sclk else None,

@@ -31,6 +31,16 @@ extern "C" {
  * 0 = the default layer of rtl_sparse_linear). */
 #define RTL_LAYER_DENSE 0x100u
 
+/* Hint OR-ed into a mode: the layer's weights are not expected in the
+ * caches (a model whose layers each run once per forward pass streams its
+ * weights through the 256 MB last-level cache between two calls of the same
+ * layer).  A sparse layer then runs the GEMM instance that probes the W
+ * lines into L2 a few k-steps ahead of their copies: the same arithmetic and
+ * the same output bits, faster with W in HBM only, slower with W already
+ * cached.  Applies to the ring shapes (r % 8 == 0, K % 8 == 0); dense
+ * layers and other shapes ignore it. */
+#define RTL_LAYER_STREAM_W 0x200u
+
 /*
  * rtl_layer_linear - one linear layer of a model under a layer-skip policy.
  *
@@ -47,8 +57,8 @@ extern "C" {
  *
  * Errors: layer_modes NULL with num_layers > 0 gives RTL_ERR_NULL_POINTER;
  * num_layers < 0 or layer outside [0, num_layers) gives RTL_ERR_BAD_SHAPE; a
- * mode that is neither RTL_LAYER_DENSE nor a valid variant gives
- * RTL_ERR_BAD_FLAGS.  All before any HIP call.
+ * mode that is neither RTL_LAYER_DENSE nor a valid variant, with or without
+ * RTL_LAYER_STREAM_W, gives RTL_ERR_BAD_FLAGS.  All before any HIP call.
  */
 rtl_status rtl_layer_linear(const uint32_t* layer_modes, int64_t num_layers, int64_t layer,
                             const uint16_t* x, const uint16_t* w,

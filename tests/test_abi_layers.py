@@ -47,6 +47,20 @@ def test_rejects_bad_tables_and_modes():
     assert _ll(_modes(0x10), 1, 0) == FLAGS
     assert _ll(_modes(0xC), 1, 0) == FLAGS          # LoRA-input field 3 is no variant
     assert _ll(_modes(0x101), 1, 0) == FLAGS        # dense is not combined with a variant
+    assert _ll(_modes(0x400), 1, 0) == FLAGS        # no such hint
+    assert _ll(_modes(layers.STREAM_W | 0xC), 1, 0) == FLAGS
+    assert _ll(_modes(layers.STREAM_W | 0x101), 1, 0) == FLAGS
+
+
+def test_stream_hint_is_accepted_on_every_mode():
+    for mode in (0, rtl.COMP_GROUP | rtl.LORA_INPUT, layers.DENSE):
+        ms = _modes(mode | layers.STREAM_W)
+        assert _ll(ms, 1, 0, k=6) == SHAPE
+        assert _ll(ms, 1, 0, y=P5 + 2) == MISAL
+        if mode != layers.DENSE:
+            assert _ll(ms, 1, 0, wsb=16) == WS
+        if _no_gpu():
+            assert _ll(ms, 1, 0) == NODEV
 
 
 def test_sparse_modes_validate_like_the_sparse_path():
@@ -78,3 +92,7 @@ def test_policy_object():
         p.mode(5)
     with pytest.raises(IndexError):
         layers.LayerPolicy(2, dense=(2,))
+    s = layers.LayerPolicy(3, dense=(1,), stream_weights=True)
+    assert [s.mode(i) for i in range(3)] == [layers.STREAM_W, layers.DENSE | layers.STREAM_W, layers.STREAM_W]
+    s = layers.LayerPolicy(3, variants={0: rtl.COMP_NONE}, stream_weights=(0, 2))
+    assert [s.mode(i) for i in range(3)] == [rtl.COMP_NONE | layers.STREAM_W, 0, layers.STREAM_W]
