@@ -27,11 +27,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveM = 128, kWaveN = 64;
 constexpr int kRB = kWaveM / 16, kCB = kWaveN / 16;
 
-// MF32: v_mfma_f32_32x32x16_bf16 on 32 x 32 blocks (4 x 2 per wavefront,
-// four 16-channel substeps per k-step) instead of v_mfma_f32_16x16x32_bf16 on
-// 16 x 16 blocks (8 x 4 per wavefront, two 32-channel halves): the same
-// products, the same LDS operand bytes, fewer and longer matrix instructions.
-template <int KM, bool MF32>
+template <int KM>
 __global__ void __launch_bounds__(kThreads, 1)
 dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                   int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y) {
@@ -51,22 +47,11 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
   const int64_t m0 = tm * kTileM;
   const int64_t ksteps = (K + kTileK - 1) / kTileK;
 
-  constexpr int kRB32 = kWaveM / 32, kCB32 = kWaveN / 32;
-  f32x4 acc[MF32 ? 1 : kRB][MF32 ? 1 : kCB];
-  f32x16 acc32[MF32 ? kRB32 : 1][MF32 ? kCB32 : 1];
-  if constexpr (MF32) {
+  f32x4 acc[kRB][kCB];
 #pragma unroll
-    for (int i = 0; i < kRB32; ++i)
+  for (int i = 0; i < kRB; ++i)
 #pragma unroll
-      for (int j = 0; j < kCB32; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc32[i][j][e] = 0.f;
-  } else {
-#pragma unroll
-    for (int i = 0; i < kRB; ++i)
-#pragma unroll
-      for (int j = 0; j < kCB; ++j) acc[i][j] = (f32x4){0, 0, 0, 0};
-  }
+    for (int j = 0; j < kCB; ++j) acc[i][j] = (f32x4){0, 0, 0, 0};
 
   // Rows past M / N lie past the end of X / W and read as zeros; channels
   // past K are pointed out of range in the tail modes.
@@ -79,13 +64,6 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
   const char* b_base1 = lds_w + wn * kCB * 2048 + f1;
   const char* a_base0 = lds_a + wm * kRB * 2048 + f0;
   const char* a_base1 = lds_a + wm * kRB * 2048 + f1;
-  // 32 x 32 operands: lane l reads row l % 32 of a block, channels
-  // 16 j + 8 (l / 32) + [0, 8) of substep j (chunk 2 j + l / 32, swizzled).
-  const int lane = threadIdx.x & 63;
-  const uint32_t row32 = (uint32_t)(lane & 31) * 128u;
-  const char* a32 = lds_a + wm * kWaveM * 128 + row32;
-  const char* b32 = lds_w + wn * kWaveN * 128 + row32;
-  auto slot32 = [&](int j) -> uint32_t { return (uint32_t)(((2 * j + (lane >> 5)) ^ (lane & 7)) << 4); };
   constexpr int kTileOps = KM == kAligned8 ? 128 / kWaves : 32 / kWaves;
 
   // Both tile copies are issued as inline-asm DMA blocks: no vector-memory
@@ -117,27 +95,6 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
     copy_tile(xr, xo, m0, M, ka, lds_a + (1 - ba) * kTileBytes);
     copy_tile(wr, wo, n0, N, kw, lds_w + (bw + 2) % kWStages * kTileBytes);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MF32) {
-      const char* as = a32 + ba * kTileBytes;
-      const char* bs = b32 + bw * kTileBytes;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t sl = slot32(j);
-        bf16x8 af[kRB32], bf[kCB32];
-#pragma unroll
-        for (int rb = 0; rb < kRB32; ++rb)
-          af[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + rb * 4096 + sl));
-#pragma unroll
-        for (int cb = 0; cb < kCB32; ++cb)
-          bf[cb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + cb * 4096 + sl));
-#pragma unroll
-        for (int rb = 0; rb < kRB32; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < kCB32; ++cb)
-            acc32[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb], bf[cb], acc32[rb][cb], 0, 0, 0);
-      }
-      return;
-    }
     const char* bs0 = b_base0 + bw * kTileBytes;
     const char* bs1 = b_base1 + bw * kTileBytes;
     const char* as0 = a_base0 + ba * kTileBytes;
@@ -191,13 +148,8 @@ dense_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w
   wait_vm<0>();
   barrier_no_fence();                     // every wave is done with the rings
 
-  if constexpr (MF32) {
-    if (N % 8 == 0) store_tile32_via_lds<kRB32, kCB32>(acc32, lds, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
-    else store_acc32_bf16<kRB32, kCB32>(acc32, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
-  } else {
-    if (N % 8 == 0) store_tile_via_lds<kRB, kCB>(acc, lds, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
-    else store_acc_bf16<kRB, kCB>(acc, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
-  }
+  if (N % 8 == 0) store_tile_via_lds<kRB, kCB>(acc, lds, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
+  else store_acc_bf16<kRB, kCB>(acc, y, M, N, m0 + wm * kWaveM, n0 + wn * kWaveN);
 }
 
 }  // namespace
@@ -206,12 +158,12 @@ hipError_t launch_dense_gemm(const uint16_t* x, const uint16_t* w, int64_t M, in
                              int64_t K, uint16_t* y, hipStream_t stream) {
   const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
   const dim3 grid((unsigned)tiles), block(kThreads);
-  // 16 x 16 blocks: the 32 x 32 form of the same loop measured 8 % slower
-  // (253 against 235 us at M = 4096, K = 3072, N = 12288).
-  constexpr bool kMf32 = false;
-  auto* k = K % kTileK == 0 ? &dense_gemm_kernel<kFullK, kMf32>
-            : K % 8 == 0   ? &dense_gemm_kernel<kAligned16, kMf32>
-                           : &dense_gemm_kernel<kAligned8, kMf32>;
+  // 16 x 16 blocks: a form of the same loop on v_mfma_f32_32x32x16_bf16
+  // (4 x 2 blocks of 32 x 32 per wavefront) measured 8 % slower (253
+  // against 235 us at M = 4096, K = 3072, N = 12288).
+  auto* k = K % kTileK == 0 ? &dense_gemm_kernel<kFullK>
+            : K % 8 == 0   ? &dense_gemm_kernel<kAligned16>
+                           : &dense_gemm_kernel<kAligned8>;
   return launch(k, grid, block, stream, x, w, M, N, K, y);
 }
 

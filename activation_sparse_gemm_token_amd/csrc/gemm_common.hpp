@@ -303,52 +303,6 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[RB][CB], c
   flush_staged_region<RB, CB>(region, y, M, N, m0, n0);
 }
 
-// The same for accumulators of 32 x 32 blocks (v_mfma_f32_32x32x16_bf16):
-// lane l holds column l % 32 of rows 8 (i / 4) + 4 (l / 32) + i % 4, i < 16.
-// The wavefront's tile is (32 RB) x (32 CB).
-template <int RB, int CB>
-__device__ __forceinline__ void store_tile32_via_lds(const f32x16 (&acc)[RB][CB], char* lds_base,
-                                                     uint16_t* __restrict__ y, int64_t M, int64_t N,
-                                                     int64_t m0, int64_t n0) {
-  constexpr int kPitch = store_pitch<2 * CB>();
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  char* region = lds_base + wave * 32 * RB * kPitch;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const int row = 32 * rb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3), col = 32 * cb + (lane & 31);
-        const uint32_t p = cvt_pk_bf16(acc[rb][cb][i], acc[rb][cb][i + 1]);
-        *reinterpret_cast<uint16_t*>(region + row * kPitch + 2 * col) = (uint16_t)p;
-        *reinterpret_cast<uint16_t*>(region + (row + 1) * kPitch + 2 * col) = (uint16_t)(p >> 16);
-      }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  flush_staged_region<2 * RB, 2 * CB>(region, y, M, N, m0, n0);
-}
-
-// Stores a wavefront's (32 RB) x (32 CB) accumulators of 32 x 32 blocks as
-// bf16, one element per lane and store (any N).
-template <int RB, int CB>
-__device__ __forceinline__ void store_acc32_bf16(const f32x16 (&acc)[RB][CB], uint16_t* __restrict__ y,
-                                                 int64_t M, int64_t N, int64_t m0, int64_t n0) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int64_t n = n0 + 32 * cb + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const uint32_t p = cvt_pk_bf16(acc[rb][cb][i], acc[rb][cb][i + 1]);
-        const int64_t m = m0 + 32 * rb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (m < M && n < N) y[m * N + n] = (uint16_t)p;
-        if (m + 1 < M && n < N) y[(m + 1) * N + n] = (uint16_t)(p >> 16);
-      }
-    }
-}
-
 // Vector-memory operations (buffer stores) store_tile_via_lds_passes
 // issues per wavefront: per pass, the 16 PRB x 2 CB chunks of 16 bytes,
 // 64 per store.
