@@ -34,7 +34,7 @@ from scipy.special import erf
 __all__ = [
     "Config", "CONFIGS", "config", "make_config", "f32_to_bf16_bits",
     "mixture_bernoulli", "mixture_exact_count", "gelu_of_normal",
-    "gaussian_bits", "tie_heavy", "at_most_two_nonzero",
+    "gaussian_bits", "tie_heavy", "at_most_two_nonzero", "uniform_bits",
 ]
 
 
@@ -102,6 +102,20 @@ def at_most_two_nonzero(rng, m: int, k: int) -> np.ndarray:
     slot = np.argsort(np.argsort(rng.random((m, k // 4, 4)), axis=2), axis=2)
     z[slot >= n_nz] = 0.0
     return f32_to_bf16_bits(z.reshape(m, k))
+
+
+def uniform_bits(rng, shape, emax: int = 0, span: int = 6) -> np.ndarray:
+    """bf16 bit patterns drawn directly, for tensors of a billion elements:
+    random sign and 7-bit mantissa, exponent uniform over the `span`
+    binades below 2^emax (magnitudes in [2^(emax - span), 2^emax)).  Fast
+    (integer draws only), so the largest tensors the interface admits can
+    be made in seconds."""
+    shape = tuple(int(v) for v in np.atleast_1d(shape))
+    bits = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    exp = (np.uint16(127 + emax - span) + (bits >> np.uint16(7)) % np.uint16(span)).astype(np.uint16)
+    sign_mant = rng.integers(0, 1 << 8, size=shape, dtype=np.uint16)
+    return (((sign_mant & np.uint16(0x80)) << np.uint16(8)) | (exp << np.uint16(7))
+            | (sign_mant & np.uint16(0x7F))).astype(np.uint16)
 
 
 @dataclasses.dataclass(frozen=True)
