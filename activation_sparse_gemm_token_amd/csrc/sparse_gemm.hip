@@ -474,8 +474,11 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   // from LDS (the last column block's W fragments included) and waited for
   // its own copies of the next step (only those of the step after may still
   // be in flight).  After it, stage o_nxt is complete for every wave and
-  // stage o_cur is free: it is refilled at once with the step three ahead,
-  // while the step's last MFMAs run.  A copy thus has two steps to land.
+  // stage o_cur is free: it is refilled with the step three ahead, at once
+  // while the step's last MFMAs run (a copy then has two steps to land), or
+  // by the second wavefront of each SIMD after column block 1 of the next
+  // k-step (late refill, 256-column tiles: 1.5 steps to land, still before
+  // the next barrier, so the waits count the same operations).
   // after_stores: the previous tile's output stores were issued after the
   // awaited copies and may still be in flight (vmcnt counts them too).
   constexpr int kStoreOps = store_passes_ops<kRB, kCB, 2>();
@@ -512,13 +515,26 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
 
   f32x4 acc[kRB][kCB];
 
+  // Late refill.  A refill burst holds its wavefront in issue while the
+  // copy path drains; when both wavefronts of a SIMD (waves w and w + 4)
+  // burst after the same barrier, its matrix core idles.  With 256-column
+  // tiles waves 4-7 therefore issue the refill of the stage a k-step
+  // consumed after column block 1 of the next k-step (3-4 % faster at the
+  // 12288-column layers; with 192-column tiles, whose copies are shorter,
+  // it measured slower and is not used).
+  const bool late_wave = CB == 4 && wave >= 4;
+  bool late_pending = false;
+  uint32_t late_stage = 0;
+
   // One k-step: 32 structured-sparse MFMAs, the W fragments (two 16-byte
   // halves per lane, swizzled tile) read one column block ahead.  The
   // position fields of row blocks 2j and 2j+1 share a 32-bit word (abid).
   // The last column block runs after the step's barrier, together with the
   // reads of the next step's first operands and the refill (deferred to the
-  // epilogue on a tile's last step, whose stage the epilogue uses).
-  auto kstep = [&](int64_t scales_for, bool after_stores, bool defer) {
+  // epilogue on a tile's last step, whose stage the epilogue uses; late, if
+  // late_ok, for waves 4-7: the next step is then a k-step of the tile, which
+  // issues it).
+  auto kstep = [&](int64_t scales_for, bool after_stores, bool defer, bool late_ok) {
     const char* s0 = b_base0 + o_cur;
     const char* s1 = b_base1 + o_cur;
     const uint32_t on = o_nxt;
@@ -532,6 +548,12 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
         for (int rb = 0; rb < kRB; rb += 2) {
           acc[rb][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb], bf, acc[rb][cb], (int)iw[rb / 2], 0, 0);
           acc[rb + 1][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb + 1], bf, acc[rb + 1][cb], (int)iw[rb / 2], 0, 1);
+        }
+        if (cb == 1 && late_pending) {
+          __builtin_amdgcn_sched_barrier(0);
+          prefetch(late_stage);
+          __builtin_amdgcn_sched_barrier(0);
+          late_pending = false;
         }
       } else {
         step_barrier(after_stores);
@@ -555,7 +577,14 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (!defer) refill(scales_for);
+        if (!defer) {
+          if (late_wave && late_ok) {
+            late_pending = true;
+            late_stage = o_cur;
+          } else {
+            refill(scales_for);
+          }
+        }
       }
     }
     if (defer && scales_for >= 0) copy_scales(scales_for);
@@ -618,10 +647,12 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     // step leaves its refill to the epilogue.
     const int64_t next_scales = i + 1 < my_tiles ? i + 1 : -1;
     const bool after_stores = i > 0 && N % 8 == 0;
-    kstep(next_scales, after_stores, lsteps == 0 && ksteps == 1);
+    // Late refills only from the middle k-steps, whose next step is a k-step
+    // of the tile: none is pending across a LoRA step or the epilogue.
+    kstep(next_scales, after_stores, lsteps == 0 && ksteps == 1, false);
 #pragma nounroll
-    for (int ks = 1; ks < ksteps - 1; ++ks) kstep(-1, false, false);
-    if (ksteps > 1) kstep(-1, false, lsteps == 0);
+    for (int ks = 1; ks < ksteps - 1; ++ks) kstep(-1, false, false, true);
+    if (ksteps > 1) kstep(-1, false, lsteps == 0, false);
     if constexpr (RING) {
       for (int g = 0; g < lsteps; ++g) lstep(g == lsteps - 1);
     }
