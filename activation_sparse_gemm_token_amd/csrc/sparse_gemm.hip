@@ -476,9 +476,9 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   // be in flight).  After it, stage o_nxt is complete for every wave and
   // stage o_cur is free: it is refilled with the step three ahead, at once
   // while the step's last MFMAs run (a copy then has two steps to land), or
-  // by the second wavefront of each SIMD after column block 1 of the next
-  // k-step (late refill, 256-column tiles: 1.5 steps to land, still before
-  // the next barrier, so the waits count the same operations).
+  // by the second wavefront of each SIMD after an early column block of the
+  // next k-step (late refill: still before the next barrier, so the waits
+  // count the same operations).
   // after_stores: the previous tile's output stores were issued after the
   // awaited copies and may still be in flight (vmcnt counts them too).
   constexpr int kStoreOps = store_passes_ops<kRB, kCB, 2>();
@@ -517,12 +517,13 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
 
   // Late refill.  A refill burst holds its wavefront in issue while the
   // copy path drains; when both wavefronts of a SIMD (waves w and w + 4)
-  // burst after the same barrier, its matrix core idles.  With 256-column
-  // tiles waves 4-7 therefore issue the refill of the stage a k-step
-  // consumed after column block 1 of the next k-step (3-4 % faster at the
-  // 12288-column layers; with 192-column tiles, whose copies are shorter,
-  // it measured slower and is not used).
-  const bool late_wave = CB == 4 && wave >= 4;
+  // burst after the same barrier, its matrix core idles.  Waves 4-7
+  // therefore issue the refill of the stage a k-step consumed after column
+  // block kLateCb of the next k-step: 1 with 256-column tiles, 0 with
+  // 192-column tiles (each measured 3-4 % and 2.5 % faster than no late
+  // refill; the other choice of block was slower for either width).
+  constexpr int kLateCb = CB == 4 ? 1 : 0;
+  const bool late_wave = wave >= 4;
   bool late_pending = false;
   uint32_t late_stage = 0;
 
@@ -549,7 +550,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
           acc[rb][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb], bf, acc[rb][cb], (int)iw[rb / 2], 0, 0);
           acc[rb + 1][cb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[rb + 1], bf, acc[rb + 1][cb], (int)iw[rb / 2], 0, 1);
         }
-        if (cb == 1 && late_pending) {
+        if (cb == kLateCb && late_pending) {
           __builtin_amdgcn_sched_barrier(0);
           prefetch(late_stage);
           __builtin_amdgcn_sched_barrier(0);
