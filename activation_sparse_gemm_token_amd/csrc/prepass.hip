@@ -797,7 +797,7 @@ hipError_t launch_prepass_t(const uint16_t* x, const uint16_t* lora_a, int64_t M
     const bool fold = comp == kCompGroup;
     if (r > 0 && ncb <= 4) {
       using Kern = decltype(&prepass_dma_kernel<2, true, true>);
-static constexpr Kern kDma[2][2][2] = {
+      static constexpr Kern kDma[2][2][2] = {
           {{&prepass_dma_kernel<2, false, false>, &prepass_dma_kernel<2, false, true>},
            {&prepass_dma_kernel<2, true, false>, &prepass_dma_kernel<2, true, true>}},
           {{&prepass_dma_kernel<4, false, false>, &prepass_dma_kernel<4, false, true>},

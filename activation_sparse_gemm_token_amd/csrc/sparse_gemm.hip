@@ -527,7 +527,7 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   bool late_pending = false;
   uint32_t late_stage = 0;
 
-  // One k-step: 32 structured-sparse MFMAs, the W fragments (two 16-byte
+  // One k-step: 8 CB structured-sparse MFMAs, the W fragments (two 16-byte
   // halves per lane, swizzled tile) read one column block ahead.  The
   // position fields of row blocks 2j and 2j+1 share a 32-bit word (abid).
   // The last column block runs after the step's barrier, together with the
@@ -593,8 +593,8 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   };
 
   // One LoRA step: for each half (hi, lo) of alpha T / s, 8 row fragments
-  // and 4 B fragments from LDS, 32 dense MFMAs; the barrier comes once the
-  // lo half is read, the refill behind it.
+  // and CB B fragments from LDS, 8 CB dense MFMAs; the barrier comes once
+  // the lo half is read, the refill behind it.
   auto lstep = [&](bool defer) {
     const char* st = &lds[0] + o_cur + 16 * lane;
     bf16x8 bfr[kCB];

@@ -62,12 +62,14 @@ def test_policy_dispatch_is_bit_exact():
 
 
 @pytest.mark.parametrize("shape", [(300, 1024, 520, 64), (4096, 3072, 12288, 64), (1152, 3072, 3072, 64),
-                                   (257, 1032, 768, 32), (64, 1028, 200, 16), (200, 2048, 1000, 8)],
+                                   (257, 1032, 768, 32), (64, 1028, 200, 16), (200, 2048, 1000, 8),
+                                   (8000, 520, 3000, 32)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_streamed_weights_hint_changes_no_bit(shape):
-    """The probing GEMM instance (256- and 192-column tiles, K % 128 == 0 and
-    only K % 8 == 0, ragged N) against the default one: identical outputs;
-    a shape outside the ring (r % 8 != 0, K % 8 == 4) ignores the hint."""
+    """The probing GEMM instance (256- and 192-column tiles, one or several
+    per workgroup, K % 128 == 0 and only K % 8 == 0, ragged N) against the
+    default one: identical outputs; a shape outside the ring (r % 8 != 0,
+    K % 8 == 4) ignores the hint."""
     m, k, n, r = shape
     print(f"[layer-skip] streamed weights M={m} K={k} N={n} r={r}", file=sys.stderr, flush=True)
     rng = np.random.default_rng(m + k + n + r)

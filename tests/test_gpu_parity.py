@@ -524,3 +524,22 @@ def test_ragged_wide_tiles(shape):
     b = gen.gaussian_bits(rng, (n, r), 0.01)
     y = run_sparse_linear(x, w, a, b)
     assert_all_rows_close(y, oracle.sparse_linear_ref(x, w, a, b), f"ragged wide {shape}")
+
+
+@pytest.mark.parametrize("shape", [(8000, 520, 3000, 32), (8192, 512, 3072, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_narrow_tiles_several_per_workgroup(shape):
+    """192-column tiles with two tiles per persistent workgroup on 256 CUs
+    (512 tiles of 256 x 192 against 384 of 256 x 256: two rounds either
+    way, so the narrower tile is taken): the cross-tile copy pipeline, the
+    staged epilogue and the staggered refills of the 192-column instance,
+    in the channel-tail and the full-K copy modes."""
+    m, k, n, r = shape
+    say(f"[parity] narrow tiles M={m} K={k} N={n} r={r}")
+    rng = np.random.default_rng(m + k + n)
+    x = gen.mixture_bernoulli(rng, m, k)
+    w = gen.gaussian_bits(rng, (n, k), 0.02)
+    a = gen.gaussian_bits(rng, (r, k), 0.01)
+    b = gen.gaussian_bits(rng, (n, r), 0.01)
+    y = run_sparse_linear(x, w, a, b)
+    assert_all_rows_close(y, oracle.sparse_linear_ref(x, w, a, b), f"narrow tiles {shape}")
