@@ -2,7 +2,8 @@
 activation-sparse linear layer.
 
 Argument marshalling only: every step of the layer runs in the HIP kernels
-of ``librtlynx.so``; PyTorch supplies device memory and the current stream.
+of ``librtlynx.so``; PyTorch supplies device memory and the current stream of
+the inputs' device (made current for the call).
 There is no fallback: if the library is missing or the device is not gfx950
 the calls raise.
 
@@ -36,7 +37,7 @@ library_path = os.path.join(_HERE, "librtlynx.so")
 STATUS = {
     0: "RTL_OK", 1: "RTL_ERR_NULL_POINTER", 2: "RTL_ERR_BAD_SHAPE", 3: "RTL_ERR_MISALIGNED",
     4: "RTL_ERR_WORKSPACE", 5: "RTL_ERR_NO_DEVICE", 6: "RTL_ERR_UNSUPPORTED_ARCH",
-    7: "RTL_ERR_HIP", 8: "RTL_ERR_BAD_FLAGS",
+    7: "RTL_ERR_HIP", 8: "RTL_ERR_BAD_FLAGS", 9: "RTL_ERR_STREAM_DEVICE",
 }
 FOLD_SCALE = 0x1
 MAX_LORA_RANK = 128
@@ -130,6 +131,16 @@ def _stream():
     return _torch().cuda.current_stream().cuda_stream
 
 
+def _on(device, **tensors):
+    """Context in which a call runs: every named tensor on ``device`` (the
+    kernels run on one device), which is made current, so that the current
+    stream and the library's device are the tensors'."""
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+    return _torch().cuda.device(device)
+
+
 def _out(out, m: int, n: int, lead, device):
     """A caller's output tensor, or a new one: the kernels write m * n bf16
     words through its data pointer, so it must be exactly that."""
@@ -173,9 +184,10 @@ def sparsify_2of4(x, fold_scale: bool = False, with_scale: bool = True):
     vals = torch.empty((m, k // 2), dtype=torch.bfloat16, device=x2.device)
     idx = torch.empty((m, (k // 4 + 1) // 2), dtype=torch.uint8, device=x2.device)
     scale = torch.empty((m,), dtype=torch.float32, device=x2.device) if with_scale else None
-    st = lib().rtl_sparsify_2of4(x2.data_ptr(), m, k, vals.data_ptr(), idx.data_ptr(),
-                                 scale.data_ptr() if scale is not None else None,
-                                 FOLD_SCALE if fold_scale else 0, _stream())
+    with _on(x2.device):
+        st = lib().rtl_sparsify_2of4(x2.data_ptr(), m, k, vals.data_ptr(), idx.data_ptr(),
+                                     scale.data_ptr() if scale is not None else None,
+                                     FOLD_SCALE if fold_scale else 0, _stream())
     _check(st, "rtl_sparsify_2of4")
     return vals, idx, scale
 
@@ -201,10 +213,11 @@ def sparse_linear(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.0, out=N
                              f"K={k}, N={n}")
     y = _out(out, m, n, x.shape[:-1], x2.device)
     workspace = _workspace(workspace, sparse_linear_workspace_bytes(m, k, r), x2.device)
-    st = lib().rtl_sparse_linear(
-        x2.data_ptr(), w2.data_ptr(),
-        lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None,
-        m, n, k, r, float(lora_scale), y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+    with _on(x2.device, w=w2, lora_a=lora_a, lora_b=lora_b):
+        st = lib().rtl_sparse_linear(
+            x2.data_ptr(), w2.data_ptr(),
+            lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None,
+            m, n, k, r, float(lora_scale), y.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "rtl_sparse_linear")
     return y.reshape(*x.shape[:-1], n)
 
@@ -231,9 +244,10 @@ def sparse_linear_noalloc(x, w, lora_a=None, lora_b=None, lora_scale: float = 1.
             raise ValueError(f"LoRA shapes {tuple(lora_a.shape)}, {tuple(lora_b.shape)} do not match "
                              f"K={k}, N={n}")
     y = _out(out, m, n, x.shape[:-1], x2.device)
-    st = lib().rtl_sparse_linear_noalloc(
-        x2.data_ptr(), w2.data_ptr(), lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None,
-        m, n, k, r, float(lora_scale), y.data_ptr(), _stream())
+    with _on(x2.device, w=w2, lora_a=lora_a, lora_b=lora_b):
+        st = lib().rtl_sparse_linear_noalloc(
+            x2.data_ptr(), w2.data_ptr(), lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None,
+            m, n, k, r, float(lora_scale), y.data_ptr(), _stream())
     _check(st, "rtl_sparse_linear_noalloc")
     return y.reshape(*x.shape[:-1], n)
 
@@ -260,15 +274,16 @@ def prepare(x, lora_a=None, lora_scale: float = 1.0, workspace=None, variant: in
         if lora_a.shape[1] != k:
             raise ValueError(f"lora_a has {lora_a.shape[1]} input channels, x has {k}")
     workspace = _workspace(workspace, sparse_linear_workspace_bytes(m, k, r), x2.device)
-    if variant:
-        st = lib().rtl_sparse_linear_prepare_variant(x2.data_ptr(), lora_a.data_ptr() if r else None, m, k, r,
-                                                     float(lora_scale), int(variant), workspace.data_ptr(),
-                                                     workspace.numel(), _stream())
-        _check(st, "rtl_sparse_linear_prepare_variant")
-    else:
-        st = lib().rtl_sparse_linear_prepare(x2.data_ptr(), lora_a.data_ptr() if r else None, m, k, r,
-                                             float(lora_scale), workspace.data_ptr(), workspace.numel(), _stream())
-        _check(st, "rtl_sparse_linear_prepare")
+    with _on(x2.device, lora_a=lora_a):
+        if variant:
+            st = lib().rtl_sparse_linear_prepare_variant(x2.data_ptr(), lora_a.data_ptr() if r else None, m, k,
+                                                         r, float(lora_scale), int(variant), workspace.data_ptr(),
+                                                         workspace.numel(), _stream())
+        else:
+            st = lib().rtl_sparse_linear_prepare(x2.data_ptr(), lora_a.data_ptr() if r else None, m, k, r,
+                                                 float(lora_scale), workspace.data_ptr(), workspace.numel(),
+                                                 _stream())
+    _check(st, "rtl_sparse_linear_prepare_variant" if variant else "rtl_sparse_linear_prepare")
     return Prepared(workspace, m, k, r, tuple(x.shape[:-1]))
 
 
@@ -287,9 +302,10 @@ def apply(prep: Prepared, w, lora_b=None, out=None):
     if w2.device != prep.workspace.device:
         raise ValueError(f"w is on {w2.device}, the prepared activation on {prep.workspace.device}")
     y = _out(out, prep.m, n, prep.lead_shape, w2.device)
-    st = lib().rtl_sparse_linear_apply(prep.workspace.data_ptr(), prep.workspace.numel(), w2.data_ptr(),
-                                       lora_b.data_ptr() if prep.r else None, prep.m, n, prep.k, prep.r,
-                                       y.data_ptr(), _stream())
+    with _on(w2.device, lora_b=lora_b if prep.r else None):
+        st = lib().rtl_sparse_linear_apply(prep.workspace.data_ptr(), prep.workspace.numel(), w2.data_ptr(),
+                                           lora_b.data_ptr() if prep.r else None, prep.m, n, prep.k, prep.r,
+                                           y.data_ptr(), _stream())
     _check(st, "rtl_sparse_linear_apply")
     return y.reshape(*prep.lead_shape, n)
 
@@ -312,10 +328,11 @@ def sparse_linear_compressed(vals, idx, scale, w, out=None, workspace=None):
         raise ValueError("scale must be a float32 device tensor [M] or None")
     y = _out(out, m, n, (m,), w2.device)
     workspace = _workspace(workspace, sparse_linear_workspace_bytes(m, k, 0), w2.device)
-    st = lib().rtl_sparse_linear_compressed(v2.data_ptr(), idx.data_ptr(),
-                                            scale.data_ptr() if scale is not None else None,
-                                            w2.data_ptr(), m, n, k, y.data_ptr(), workspace.data_ptr(),
-                                            workspace.numel(), _stream())
+    with _on(w2.device, vals=v2, idx=idx, scale=scale):
+        st = lib().rtl_sparse_linear_compressed(v2.data_ptr(), idx.data_ptr(),
+                                                scale.data_ptr() if scale is not None else None,
+                                                w2.data_ptr(), m, n, k, y.data_ptr(), workspace.data_ptr(),
+                                                workspace.numel(), _stream())
     _check(st, "rtl_sparse_linear_compressed")
     return y
 
@@ -329,6 +346,7 @@ def dense_linear(x, w, out=None):
     if w2.shape[1] != k:
         raise ValueError(f"w has {w2.shape[1]} input channels, x has {k}")
     y = _out(out, m, n, x.shape[:-1], x2.device)
-    st = lib().rtl_dense_linear(x2.data_ptr(), w2.data_ptr(), m, n, k, y.data_ptr(), _stream())
+    with _on(x2.device, w=w2):
+        st = lib().rtl_dense_linear(x2.data_ptr(), w2.data_ptr(), m, n, k, y.data_ptr(), _stream())
     _check(st, "rtl_dense_linear")
     return y.reshape(*x.shape[:-1], n)

@@ -53,8 +53,9 @@ bool layer_sizes_ok(int64_t M, int64_t N, int64_t K, int64_t r) {
   return bytes_ok(L.mp, L.kp, 1) && bytes_ok(L.mp, L.rp, 4);
 }
 
-// Checks that a gfx950 device is current; sets *cus to its CU count.
-rtl_status check_device(int* cus = nullptr) {
+// Checks that a gfx950 device is current and that `stream` (NULL: the null
+// stream) belongs to it; sets *cus to its CU count.
+rtl_status check_device(hipStream_t stream, int* cus = nullptr) {
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
     (void)hipGetLastError();
@@ -64,6 +65,16 @@ rtl_status check_device(int* cus = nullptr) {
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return RTL_ERR_NO_DEVICE;
+  }
+  if (stream != nullptr) {
+    // The kernels run on the stream's device with the current device's
+    // launch parameters (and, without a workspace, its scratch array).
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return RTL_ERR_HIP;
+    }
+    if (sdev != dev) return RTL_ERR_STREAM_DEVICE;
   }
   if (dev < 0 || dev >= kMaxDevices) return RTL_ERR_UNSUPPORTED_ARCH;
   int known = g_arch_ok[dev].load(std::memory_order_relaxed);
@@ -121,7 +132,7 @@ RTL_API rtl_status rtl_sparsify_2of4(const uint16_t* x, int64_t M, int64_t K, ui
   if (x == nullptr || vals == nullptr || idx == nullptr) return RTL_ERR_NULL_POINTER;
   if (!aligned16(x) || !aligned16(vals) || !aligned16(idx) || (scale != nullptr && !aligned16(scale)))
     return RTL_ERR_MISALIGNED;
-  const rtl_status d = check_device();
+  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream));
   if (d != RTL_OK) return d;
   return from_hip(rtl::launch_sparsify_2of4(x, M, K, vals, idx, scale, (flags & RTL_FOLD_SCALE) != 0,
                                             static_cast<hipStream_t>(hip_stream)));
@@ -144,7 +155,7 @@ RTL_API rtl_status rtl_sparse_linear_prepare(const uint16_t* x, const uint16_t* 
   if (!aligned16(x) || (r > 0 && !aligned16(lora_a))) return RTL_ERR_MISALIGNED;
   if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
-  const rtl_status d = check_device();
+  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream));
   if (d != RTL_OK) return d;
   return from_hip(rtl::launch_prepass(x, r > 0 ? lora_a : nullptr, M, K, r, lora_scale, workspace,
                                       static_cast<hipStream_t>(hip_stream)));
@@ -163,7 +174,7 @@ RTL_API rtl_status rtl_sparse_linear_prepare_variant(const uint16_t* x, const ui
   if (!aligned16(x) || (r > 0 && !aligned16(lora_a))) return RTL_ERR_MISALIGNED;
   if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
-  const rtl_status d = check_device();
+  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream));
   if (d != RTL_OK) return d;
   return from_hip(rtl::launch_prepass(x, r > 0 ? lora_a : nullptr, M, K, r, lora_scale, workspace,
                                       static_cast<hipStream_t>(hip_stream), (int)comp, (int)lora));
@@ -183,7 +194,7 @@ rtl_status apply_impl(const void* workspace, size_t workspace_bytes, const uint1
   if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
   int cus = 0;
-  const rtl_status d = check_device(&cus);
+  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream), &cus);
   if (d != RTL_OK) return d;
   return from_hip(rtl::launch_sparse_gemm(workspace, w, r > 0 ? lora_b : nullptr, M, N, K, r, y, cus,
                                           static_cast<hipStream_t>(hip_stream), 0, prefetch_w));
@@ -212,7 +223,7 @@ RTL_API rtl_status rtl_sparse_linear(const uint16_t* x, const uint16_t* w, const
   if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, r).total) return RTL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
   int cus = 0;
-  const rtl_status d = check_device(&cus);
+  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream), &cus);
   if (d != RTL_OK) return d;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (rtl::launch_prepass(x, r > 0 ? lora_a : nullptr, M, K, r, lora_scale, workspace, stream) != hipSuccess)
@@ -232,7 +243,7 @@ RTL_API rtl_status rtl_sparse_linear_noalloc(const uint16_t* x, const uint16_t* 
   if (r > 0 && (!aligned16(lora_a) || !aligned16(lora_b))) return RTL_ERR_MISALIGNED;
   if (rtl::ws_layout(M, K, r).total > (size_t)RTL_NOALLOC_SCRATCH_BYTES) return RTL_ERR_WORKSPACE;
   int cus = 0;
-  const rtl_status d = check_device(&cus);
+  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream), &cus);
   if (d != RTL_OK) return d;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return RTL_ERR_NO_DEVICE;
@@ -259,7 +270,7 @@ RTL_API rtl_status rtl_sparse_linear_compressed(const uint16_t* vals, const uint
   if (workspace == nullptr || workspace_bytes < rtl::ws_layout(M, K, 0).total) return RTL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RTL_ERR_MISALIGNED;
   int cus = 0;
-  const rtl_status d = check_device(&cus);
+  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream), &cus);
   if (d != RTL_OK) return d;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const hipError_t e = rtl::launch_repack(vals, idx, scale, M, K, workspace, stream);
@@ -274,7 +285,7 @@ RTL_API rtl_status rtl_dense_linear(const uint16_t* x, const uint16_t* w, int64_
   if (M == 0 || N == 0) return RTL_OK;
   if (x == nullptr || w == nullptr || y == nullptr) return RTL_ERR_NULL_POINTER;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return RTL_ERR_MISALIGNED;
-  const rtl_status d = check_device();
+  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream));
   if (d != RTL_OK) return d;
   return from_hip(rtl::launch_dense_gemm(x, w, M, N, K, y, static_cast<hipStream_t>(hip_stream)));
 }
@@ -290,6 +301,7 @@ RTL_API const char* rtl_status_string(rtl_status s) {
     case RTL_ERR_UNSUPPORTED_ARCH: return "the current device is not gfx950 (MI355X)";
     case RTL_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case RTL_ERR_BAD_FLAGS: return "unknown flag bits";
+    case RTL_ERR_STREAM_DEVICE: return "hip_stream belongs to a device other than the current one";
   }
   return "unknown status";
 }

@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import ctypes
 
-from . import _as_2d, _check, _out, _stream, _workspace, lib, sparse_linear_workspace_bytes
+from . import _as_2d, _check, _on, _out, _stream, _workspace, lib, sparse_linear_workspace_bytes
 
 DENSE = 0x100
 STREAM_W = 0x200
@@ -85,9 +85,10 @@ class LayerPolicy:
         y = _out(out, m, n, x.shape[:-1], x2.device)
         if self.mode(layer) & ~STREAM_W != DENSE:
             workspace = _workspace(workspace, sparse_linear_workspace_bytes(m, k, r), x2.device)
-        st = _fn()(self.modes, self.num_layers, layer, x2.data_ptr(), w2.data_ptr(),
-                   lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None, m, n, k, r,
-                   float(lora_scale), y.data_ptr(), workspace.data_ptr() if workspace is not None else None,
-                   workspace.numel() if workspace is not None else 0, _stream())
+        with _on(x2.device, w=w2, lora_a=lora_a, lora_b=lora_b):
+            st = _fn()(self.modes, self.num_layers, layer, x2.data_ptr(), w2.data_ptr(),
+                       lora_a.data_ptr() if r else None, lora_b.data_ptr() if r else None, m, n, k, r,
+                       float(lora_scale), y.data_ptr(), workspace.data_ptr() if workspace is not None else None,
+                       workspace.numel() if workspace is not None else 0, _stream())
         _check(st, "rtl_layer_linear")
         return y.reshape(*x.shape[:-1], n)

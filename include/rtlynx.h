@@ -30,6 +30,9 @@
  *     allocates nothing and keeps no pointer after a call returns.
  *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronise.  Outputs must not alias inputs.
+ *   - The kernels run on the current device (hipSetDevice), and hip_stream
+ *     must belong to it, else RTL_ERR_STREAM_DEVICE; every tensor pointer
+ *     must be memory of that device.
  *   - Host threads may call the library concurrently: its only state is a
  *     per-device record of the architecture check, written atomically.  Calls
  *     that can run at the same time on the GPU (different streams with no
@@ -65,7 +68,8 @@ typedef enum {
   RTL_ERR_NO_DEVICE = 5,         /* no HIP device is visible                 */
   RTL_ERR_UNSUPPORTED_ARCH = 6,  /* the current device is not gfx950         */
   RTL_ERR_HIP = 7,               /* a HIP runtime call or launch failed      */
-  RTL_ERR_BAD_FLAGS = 8          /* unknown bits in a flags argument         */
+  RTL_ERR_BAD_FLAGS = 8,         /* unknown bits in a flags argument         */
+  RTL_ERR_STREAM_DEVICE = 9      /* hip_stream is not on the current device  */
 } rtl_status;
 
 /* rtl_sparsify_2of4 flag: store vals = bf16_rne(s * x) (the compensated

@@ -51,7 +51,7 @@ def test_only_declared_symbols_are_exported():
 
 def test_version_and_status_strings():
     assert rtl.version() == 10000
-    for code in range(9):
+    for code in range(10):
         s = rtl.status_string(code)
         assert isinstance(s, str) and s
     assert rtl.status_string(OK) == "ok"
