@@ -8,8 +8,10 @@
 
 namespace rtl {
 
+// compute_units: the device's CU count (one or two wavefronts per row).
 hipError_t launch_sparsify_2of4(const uint16_t* x, int64_t M, int64_t K, uint16_t* vals,
-                                uint8_t* idx, float* scale, bool fold, hipStream_t stream);
+                                uint8_t* idx, float* scale, bool fold, int compute_units,
+                                hipStream_t stream);
 
 // Pre-pass of the fused path: selection, compression into the structured-
 // sparse matrix-core operand order, per-token scale, LoRA-down product.

@@ -132,9 +132,10 @@ RTL_API rtl_status rtl_sparsify_2of4(const uint16_t* x, int64_t M, int64_t K, ui
   if (x == nullptr || vals == nullptr || idx == nullptr) return RTL_ERR_NULL_POINTER;
   if (!aligned16(x) || !aligned16(vals) || !aligned16(idx) || (scale != nullptr && !aligned16(scale)))
     return RTL_ERR_MISALIGNED;
-  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream));
+  int cus = 0;
+  const rtl_status d = check_device(static_cast<hipStream_t>(hip_stream), &cus);
   if (d != RTL_OK) return d;
-  return from_hip(rtl::launch_sparsify_2of4(x, M, K, vals, idx, scale, (flags & RTL_FOLD_SCALE) != 0,
+  return from_hip(rtl::launch_sparsify_2of4(x, M, K, vals, idx, scale, (flags & RTL_FOLD_SCALE) != 0, cus,
                                             static_cast<hipStream_t>(hip_stream)));
 }
 
