@@ -11,18 +11,21 @@
 //
 //   T = (X - S(X)) A^T = ((1-M)*X) A^T + (1 - s) * ((M*X) A^T)
 //
-// Both terms are 2:4-sparse products of exact input words, so they run on the
-// structured-sparse matrix cores with the kept and the pruned halves of each
-// group, and no cancellation happens in fp32.  alpha*T/s is stored as a
+// In the generic kernel both terms are 2:4-sparse products of exact input
+// words, so they run on the structured-sparse matrix cores with the kept and
+// the pruned halves of each group, and no cancellation happens in fp32; the
+// DMA-streamed kernel (r <= 64) forms X A^T - s (M*X) A^T instead (dense
+// MFMAs on the input words as loaded, no pruned operand to gather; see
+// there).  alpha*T/s is stored as a
 // bf16 hi/lo pair in the dense 16x16x32 A-operand order: divided by the
 // token's scale (s >= 1), so that the GEMM can accumulate the LoRA-up
 // product into the same fp32 accumulators as the sparse product and apply
 // s once at the end, Y = s (S(X) W^T + (alpha T / s) B^T).
 //
 // Selection happens here, once per element, and not in the GEMM prologue:
-// there it would be repeated for every N tile, and its VALU cost (about 30
-// integer instructions per group) exceeds the structured-sparse MFMA time
-// of the tile.
+// there it would be repeated for every N tile, and its VALU cost (about 48
+// lane operations per group of 4, from the instruction counters) exceeds
+// the structured-sparse MFMA time of the tile.
 //
 // Grid: one workgroup of 8 wavefronts per 16-token block; wavefront w covers
 // a contiguous range of 128-channel k-pairs.  Lane l handles token l % 16 and
