@@ -763,6 +763,7 @@ def main():
     sp_ms = time_fn(lambda: lib.rtl_sparsify_2of4(xd.data_ptr(), m, k, vals.data_ptr(), idx.data_ptr(),
                                                    scale.data_ptr(), 0, stream.cuda_stream), args.steps)
     sp_bytes = 2 * m * k + m * k + m * ((k // 4 + 1) // 2) + 4 * m
+    prep_bytes = 2 * m * k + 2 * r * k + m * k + m * k // 8 + 4 * m + 4 * m * r
     # The unfused form of the layer without LoRA: sparsify to the canonical
     # compressed X in HBM, then the GEMM on it (its repack included).
     ws0 = torch.empty((rtl.sparse_linear_workspace_bytes(m, k, 0),), dtype=torch.uint8, device=dev)
@@ -886,6 +887,8 @@ def main():
             "interleaved_us": {k: [round(v * 1e3, 2) for v in vs] for k, vs in blocks.items()},
             "inhouse_dense_tflops": round(flops_dense_eq / (dense_ms * 1e-3) / 1e12, 1),
             "hipblaslt_tflops": round(flops_dense_eq / (blas_ms * 1e-3) / 1e12, 1),
+            "inhouse_dense_frac_peak": round(flops_dense_eq / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_DENSE_TFLOPS, 4),
+            "hipblaslt_frac_peak": round(flops_dense_eq / (blas_ms * 1e-3) / 1e12 / PEAK_BF16_DENSE_TFLOPS, 4),
             "frac_dense_peak": round(value / PEAK_BF16_DENSE_TFLOPS, 4),
             "frac_sparse_peak": round(value / (2 * PEAK_BF16_DENSE_TFLOPS), 4),
             "prepare_us": round(prep_avg * 1e3, 2),
@@ -893,6 +896,10 @@ def main():
             "prepare_us_queued_calls": round(prep_queued * 1e3, 2),
             "apply_us": round(apply_avg * 1e3, 2),
             "prepare_share": round(prep_avg / (prep_avg + apply_avg), 4),
+            # the pre-pass's HBM roofline: X and A read once, the workspace
+            # (operand words, position fields, s, alpha T / s) written once
+            "prepare_alg_bytes": prep_bytes,
+            "prepare_frac_hbm": round(prep_bytes / (prep_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "sparsify_2of4_us": round(sp_ms * 1e3, 2),
             "sparsify_2of4_GBs": round(sp_bytes / (sp_ms * 1e-3) / 1e9, 1),
             "sparsify_2of4_frac_hbm": round(sp_bytes / (sp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
