@@ -543,3 +543,53 @@ def test_narrow_tiles_several_per_workgroup(shape):
     b = gen.gaussian_bits(rng, (n, r), 0.01)
     y = run_sparse_linear(x, w, a, b)
     assert_all_rows_close(y, oracle.sparse_linear_ref(x, w, a, b), f"narrow tiles {shape}")
+
+
+def _path_cases(count=40, seed=20261204):
+    """Seeded random layers over every entry point that computes the layer:
+    rtl_sparse_linear, prepare_variant + apply (a random compensation and
+    LoRA input), the allocation-free call, and the layer policy with the
+    streamed-weights hint; M up to 6000 and N up to 7000 (several tiles per
+    persistent workgroup), K a multiple of 4 or of 128, ranks 0 to 128."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        m = int(rng.choice([rng.integers(1, 300), rng.integers(256, 2600), rng.integers(2600, 6000)]))
+        k = 4 * int(rng.integers(1, 700)) if rng.random() < 0.7 else 128 * int(rng.integers(1, 20))
+        n = int(rng.choice([rng.integers(1, 2500), rng.integers(2500, 7000)]))
+        r = int(rng.choice([0, 5, 8, 16, 24, 32, 48, 64, 64, 96, 128]))
+        path = str(rng.choice(["layer", "variant", "noalloc", "stream"]))
+        comp, lora = str(rng.choice(list(COMP))), str(rng.choice(list(LORA)))
+        cases.append((i, m, k, n, r, path, comp, lora))
+    return cases
+
+
+@pytest.mark.parametrize("case", _path_cases(), ids=lambda c: f"{c[0]}-{c[5]}-{c[1]}x{c[2]}x{c[3]}x{c[4]}")
+def test_random_entry_point_sweep(case):
+    from activation_sparse_gemm_token_amd import layers
+    i, m, k, n, r, path, comp, lora = case
+    say(f"[parity] path sweep {i}: {path} M={m} K={k} N={n} r={r}" + (f" {comp}/{lora}" if path == "variant" else ""))
+    rng = np.random.default_rng(1000 + i)
+    x = gen.mixture_bernoulli(rng, m, k)
+    w = gen.gaussian_bits(rng, (n, k), 0.02)
+    a = gen.gaussian_bits(rng, (r, k), 0.01) if r else None
+    b = gen.gaussian_bits(rng, (n, r), 0.01) if r else None
+    xd, wd = to_dev(x), to_dev(w)
+    ad, bd = (to_dev(a), to_dev(b)) if r else (None, None)
+    alpha = 0.75
+    if path == "variant":
+        y = rtl.apply(rtl.prepare(xd, ad, alpha, variant=COMP[comp] | LORA[lora]), wd, bd)
+        ref = oracle.sparse_linear_variant_ref(x, w, a, b, alpha, comp=comp, lora=lora)
+    else:
+        if path == "layer":
+            y = rtl.sparse_linear(xd, wd, ad, bd, alpha)
+        elif path == "noalloc":
+            y = rtl.sparse_linear_noalloc(xd, wd, ad, bd, alpha)
+        else:
+            y = layers.LayerPolicy(1, stream_weights=True).linear(0, xd, wd, ad, bd, alpha)
+            plain = rtl.sparse_linear(xd, wd, ad, bd, alpha)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host(y), to_host(plain)), "the streamed-weights hint changed the output"
+        ref = oracle.sparse_linear_ref(x, w, a, b, alpha)
+    torch.cuda.synchronize()
+    assert_y_close(y_to_f64(y), ref, f"path sweep {i} ({path})")
