@@ -245,7 +245,7 @@ def dist(ms_list):
             "p90": round(p90 * 1e3, 2), "mean": round(sum(v) / len(v) * 1e3, 2)}
 
 
-SUITE = ("attn_proj", "mlp_up", "mlp_down", "textimg_p05", "textimg_p10", "textimg_p25",
+SUITE = ("tiny", "attn_proj", "mlp_up", "mlp_down", "textimg_p05", "textimg_p10", "textimg_p25",
          "mlp_up_share8", "textimg_share8", "textimg_share2")
 
 
@@ -269,7 +269,8 @@ def queued_ms(fn, reps: int, stream) -> float:
 
 def run_suite(reps: int, warmup: int):
     """Every linear-layer workload, warm, one JSON line each: the layer
-    (pre-pass + apply), its halves, the in-house dense GEMM and hipBLASLt;
+    (pre-pass + apply), its halves, the in-house dense GEMM, hipBLASLt and
+    the standalone sparsify;
     then Q, K and V sharing one input (one pre-pass, three applies) and the
     time-weighted speedup over one DiT block's linears (Q, K, V, output
     projection, MLP up, MLP down)."""
@@ -298,6 +299,33 @@ def run_suite(reps: int, warmup: int):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    def interleaved_ms(legs):
+        """Median time per call of each leg over BLOCKS blocks of `reps`
+        back-to-back calls, the legs' order rotated from block to block."""
+        # warm-up: the legs in turn for at least a third of RAMP_MS (the
+        # clock's ramp), and at least `warmup` calls of each
+        t0, calls = time.perf_counter(), 0
+        while calls < warmup or (time.perf_counter() - t0) * 1e3 < RAMP_MS / 3:
+            for fn in legs.values():
+                fn()
+            calls += 1
+            if calls % 10 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        order = list(legs)
+        blocks = {kk: [] for kk in legs}
+        for bi in range(BLOCKS):
+            for kk in order[bi % len(order):] + order[:bi % len(order)]:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    legs[kk]()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                blocks[kk].append(e0.elapsed_time(e1) / reps)
+        return {kk: statistics.median(v) for kk, v in blocks.items()}
+
     res = {}
     for name in SUITE:
         cfg = gen.config(name)
@@ -306,7 +334,13 @@ def run_suite(reps: int, warmup: int):
         m, k, n, r = cfg.m, cfg.k, cfg.n, cfg.r
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ws = torch.empty((rtl.sparse_linear_workspace_bytes(m, k, r),), dtype=torch.uint8, device=dev)
-        t_layer = mean_ms(lambda: rtl.sparse_linear(xd, wd, ad, bd, 1.0, out=y, workspace=ws))
+        wt = wd.t()
+        # the layer and both dense GEMMs in interleaved blocks (no leg gains
+        # from coming after the others)
+        t = interleaved_ms({"layer": lambda: rtl.sparse_linear(xd, wd, ad, bd, 1.0, out=y, workspace=ws),
+                            "dense": lambda: rtl.dense_linear(xd, wd, out=y),
+                            "blas": lambda: torch.matmul(xd, wt, out=y)})
+        t_layer, t_dense, t_blas = t["layer"], t["dense"], t["blas"]
         # the halves through the C entry points, arguments marshalled once;
         # the pre-pass (shorter than a call's host time) queued behind a wait
         clib, sp = rtl.lib(), stream.cuda_stream
@@ -314,9 +348,15 @@ def run_suite(reps: int, warmup: int):
         apply_args = (ws.data_ptr(), ws.numel(), wd.data_ptr(), bd.data_ptr(), m, n, k, r, y.data_ptr(), sp)
         prep = rtl.prepare(xd, ad, 1.0, workspace=ws)
         t_apply = mean_ms(lambda: clib.rtl_sparse_linear_apply(*apply_args))
-        t_dense = mean_ms(lambda: rtl.dense_linear(xd, wd, out=y))
-        wt = wd.t()
-        t_blas = mean_ms(lambda: torch.matmul(xd, wt, out=y))
+        # the standalone sparsify into the canonical layout, queued likewise
+        vals = torch.empty((m, k // 2), dtype=torch.bfloat16, device=dev)
+        idx = torch.empty((m, (k // 4 + 1) // 2), dtype=torch.uint8, device=dev)
+        scale = torch.empty((m,), dtype=torch.float32, device=dev)
+        sp_args = (xd.data_ptr(), m, k, vals.data_ptr(), idx.data_ptr(), scale.data_ptr(), 0, sp)
+        for _ in range(warmup):
+            clib.rtl_sparsify_2of4(*sp_args)
+        t_sp = queued_ms(lambda: clib.rtl_sparsify_2of4(*sp_args), reps, stream)
+        sp_bytes = 2 * m * k + m * k + m * ((k // 4 + 1) // 2) + 4 * m
         # last: its GPU-side wait lets the clock drop
         t_prep = queued_ms(lambda: clib.rtl_sparse_linear_prepare(*prep_args), reps, stream)
         f = 2.0 * m * n * k
@@ -326,10 +366,14 @@ def run_suite(reps: int, warmup: int):
                 "hipblaslt_us": round(t_blas * 1e3, 2),
                 "eff_tflops": round(f / (t_layer * 1e-3) / 1e12, 1),
                 "speedup_vs_inhouse_dense": round(t_dense / t_layer, 3),
-                "speedup_vs_hipblaslt": round(t_blas / t_layer, 3)}
+                "speedup_vs_hipblaslt": round(t_blas / t_layer, 3),
+                "frac_dense_peak": round(f / (t_layer * 1e-3) / 1e12 / PEAK_BF16_DENSE_TFLOPS, 4),
+                "sparsify_us": round(t_sp * 1e3, 2),
+                "sparsify_GBs": round(sp_bytes / (t_sp * 1e-3) / 1e9, 1),
+                "sparsify_frac_hbm": round(sp_bytes / (t_sp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         res[name] = line
         print(json.dumps(line), flush=True)
-        del xd, wd, ad, bd, y, ws, prep
+        del xd, wd, ad, bd, y, ws, prep, vals, idx, scale
 
     # Q, K, V: three 3072 x 3072 projections of one input sharing the
     # LoRA-down (one pre-pass), each with its own W and LoRA-up.
@@ -357,7 +401,8 @@ def run_suite(reps: int, warmup: int):
         for i in range(3):
             torch.matmul(xd, wts[i], out=ys[i])
 
-    t_s, t_d, t_b = mean_ms(qkv_sparse), mean_ms(qkv_dense), mean_ms(qkv_blas)
+    t = interleaved_ms({"s": qkv_sparse, "d": qkv_dense, "b": qkv_blas})
+    t_s, t_d, t_b = t["s"], t["d"], t["b"]
     qkv = {"workload": "qkv_shared_input", "M": cfg.m, "K": cfg.k, "N": f"3 x {cfg.n}", "r": cfg.r,
            "layer_us": round(t_s * 1e3, 2), "inhouse_dense_us": round(t_d * 1e3, 2),
            "hipblaslt_us": round(t_b * 1e3, 2),
