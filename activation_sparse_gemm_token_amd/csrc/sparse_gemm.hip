@@ -64,6 +64,7 @@ struct Tile {
   static constexpr int kWOps = CB;
   static constexpr int kStepOps = CB + 3;
   static_assert(kWaves * 32 * store_pitch<CB>() <= kStageBytes, "store staging (2 row blocks) fits one stage");
+  static_assert(kWaves * 16 * store_pitch<CB>() <= kStageBytes - kAStageOff, "1 row block fits the A region");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
@@ -173,6 +174,54 @@ __device__ __forceinline__ void dma_a_tile_asm(__amdgpu_buffer_rsrc_t ar, __amdg
       : [va] "v"(va), [vi] "v"(vi), [ar] "s"(ar), [ir] "s"(ir), [aso] "s"(a_so), [iso] "s"(i_so),
         [st] "s"(stage), [la] "s"(la), [li] "s"(li)
       : "memory", "scc");
+  (void)saved;
+}
+
+// The W tile of dma_kstep_asm alone (CB operations).
+template <int CB>
+__device__ __forceinline__ void dma_w_tile_part_asm(__amdgpu_buffer_rsrc_t wr, const uint32_t (&w)[CB],
+                                                    uint32_t w_so, uint32_t stage, uint32_t lw) {
+  uint32_t saved;
+  if constexpr (CB == 4) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_add_u32 m0, %[st], %[lw]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w0], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w1], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w2], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w3], %[wr], %[wso] offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [w0] "v"(w[0]), [w1] "v"(w[1]), [w2] "v"(w[2]), [w3] "v"(w[3]), [wr] "s"(wr), [wso] "s"(w_so),
+          [st] "s"(stage), [lw] "s"(lw)
+        : "memory", "scc");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_add_u32 m0, %[st], %[lw]\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w0], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w1], %[wr], %[wso] offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %[w2], %[wr], %[wso] offen lds\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [w0] "v"(w[0]), [w1] "v"(w[1]), [w2] "v"(w[2]), [wr] "s"(wr), [wso] "s"(w_so),
+          [st] "s"(stage), [lw] "s"(lw)
+        : "memory", "scc");
+  }
   (void)saved;
 }
 
@@ -404,10 +453,27 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     pc_wv = (uint32_t)(((pc_n0 + 8 * kCB * wave + (lane >> 3)) * K) * 2) + 2u * k_lane;
   };
   cursor_tile(0);
-  auto prefetch = [&](uint32_t st_off) {
+  // part: 0 the whole step; 1 its W tile only (a k-step of the ring in the
+  // 16-byte copy modes; the cursor stays); 2 the rest after a part 1.
+  auto prefetch = [&](uint32_t st_off, int part = 0) {
     const uint32_t st = lds_base + st_off;
     const bool kcopy = !RING || pc_loc < ksteps;
-    if (kcopy) {
+    if (part == 1) {
+      if constexpr (KM != kAligned8) {
+        uint32_t wv[kCB];
+#pragma unroll
+        for (int q = 0; q < kCB; ++q) wv[q] = pc_wv + q * row8;
+        if (KM == kAligned16 && (int64_t)pc_loc * kTileK + k_lane + 8 > K) {
+#pragma unroll
+          for (int q = 0; q < kCB; ++q) wv[q] = kOobOffset - pc_wso;
+        }
+        dma_w_tile_part_asm<kCB>(wr, wv, pc_wso, st, lw);
+      }
+      return;
+    }
+    if (part == 2) {
+      dma_a_tile_asm(ar, ir, pc_aso, pc_iso, va, vi, st, la, li);
+    } else if (kcopy) {
       if constexpr (KM == kAligned8) {
         dma_a_tile_asm(ar, ir, pc_aso, pc_iso, va, vi, st, la, li);
         dma_w_tile_dword<kWaves>(wr, N, K, pc_n0, (int64_t)pc_loc * kTileK, &lds[st_off]);
@@ -481,7 +547,12 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
   // count the same operations).
   // after_stores: the previous tile's output stores were issued after the
   // awaited copies and may still be in flight (vmcnt counts them too).
-  constexpr int kStoreOps = store_passes_ops<kRB, kCB, 2>();
+  // Epilogue staging: 1 row block per pass (16 rows x store_pitch per
+  // wavefront: 18 KiB for 8 wavefronts, the stage's A and position
+  // regions) in the ring shapes with 16-byte copies, else 2 per pass.
+  constexpr bool kEarlyW = RING && KM != kAligned8;
+  constexpr int kPRB = kEarlyW ? 1 : 2;
+  constexpr int kStoreOps = store_passes_ops<kRB, kCB, kPRB>();
   static_assert(2 * kOps + kStoreOps < 64, "vmcnt field is 6 bits");
   auto step_barrier = [&](bool after_stores) {
     __builtin_amdgcn_sched_barrier(0);
@@ -660,8 +731,13 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
 
     // Epilogue.  Every wave has passed the last step's barrier, so the
     // stage that step consumed (o_pf after the rotation) is free: the tile
-    // is staged through it before the deferred refill.  The next stage is
-    // complete and the one after is in flight.
+    // is staged through it before the deferred refill, or, when that refill
+    // is a k-step (the ring shapes with 16-byte copies), through its A
+    // region only while the refill's W tile goes out first into its W
+    // region (early W: the copy path works during the epilogue's conversion
+    // and LDS passes; 0.3-1.1 % faster at the shapes with several tiles per
+    // workgroup, outputs bit-identical).  The next stage is complete and the
+    // one after is in flight.
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!RING) {
       // LoRA-up from global memory: (alpha T / s)_hi B^T + (alpha T / s)_lo B^T.
@@ -715,19 +791,30 @@ sparse_gemm_kernel(const u32x4* __restrict__ xv, const uint16_t* __restrict__ xi
     }
 
     const int64_t m0 = tm * kTileM + wm * kWaveM;
+    const bool early_w = kEarlyW && N % 8 == 0 && pc_loc < ksteps;
     if (N % 8 == 0) {
-      char* region = &lds[0] + o_pf + wave * (32 * store_pitch<kCB>());
-      store_tile_via_lds_passes<kRB, kCB, 2>(acc, region, y, M, N, m0, n0 + wn * kWaveN);
+      if (early_w) {
+        // The deferred refill's W tile goes out now, into the W region of
+        // the free stage; the tile is staged through its A region.
+        __builtin_amdgcn_sched_barrier(0);
+        prefetch(o_pf, 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      char* region = &lds[0] + o_pf + (kEarlyW ? kAStageOff : 0) + wave * (16 * kPRB * store_pitch<kCB>());
+      store_tile_via_lds_passes<kRB, kCB, kPRB>(acc, region, y, M, N, m0, n0 + wn * kWaveN);
     } else {
       store_acc_bf16<kRB, kCB>(acc, y, M, N, m0, n0 + wn * kWaveN);
     }
-    // Every wave is done with the staging area: the deferred refill goes
-    // there.  The next tile starts from stage o_cur, complete since the
-    // last step's barrier.
+    // Every wave is done with the staging area: the deferred refill (its
+    // A tile and position fields only, after an early W) goes there.  The
+    // next tile starts from stage o_cur, complete since the last step's
+    // barrier.  The vmcnt waits count the same operations either way: the
+    // refill's copies, split or not, and the stores come before the next
+    // tile's first barrier.
     __builtin_amdgcn_sched_barrier(0);
     barrier_no_fence();
     __builtin_amdgcn_sched_barrier(0);
-    prefetch(o_pf);
+    prefetch(o_pf, early_w ? 2 : 0);
     __builtin_amdgcn_sched_barrier(0);
     if (i + 1 < my_tiles) load_first(o_cur);
   }
